@@ -1,0 +1,191 @@
+"""Benchmark of the blockwise ring-attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+the forward (ring walk, masks, online softmax, P.V) followed by the backward
+(Delta preprocess, dK/dV kernel, dQ kernel), all through the C-ABI.  The
+default workload is one device's share of a 1M-token context: ring rank 7 of
+8, 131072 local queries against 1048576 keys, 16 heads, head_dim 64, bf16,
+causal, with fully masked blocks skipped.
+
+Prints one JSON line.  value = whole-step attention TFLOP/s, counting 4*D
+(forward) + 10*D (backward) FLOPs per visible (query, key) pair.  Per-kernel
+durations come from HIP events recorded on the stream the kernels run on.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (fwd, fwd+bwd) at 1 MI355X and % of bf16 MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="share-1m-r7")
+    ap.add_argument("--fwd-only", action="store_true", help="time the forward alone (not the bench line)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, t, target_s):
+    """The float64 oracle, as it stands, on a bounded sample of the same workload: query rows of one head
+    taken in order from a seeded permutation until about target_s seconds of CPU time, each against its
+    full visible key set, forward + backward.  Returns TFLOP/s over the sample's visible pairs."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    h = 0
+    f64 = lambda x: x.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    k = f64(t["k"][:, :, h:h + 1])
+    v = f64(t["v"][:, :, h:h + 1])
+    bias = None if t["bias"] is None else f64(t["bias"][h:h + 1])
+    seg = None if t["segment_ids"] is None else t["segment_ids"].cpu().numpy()
+    qpos_all = w.q_positions()
+    perm = np.random.default_rng(5).permutation(w.q_len)
+    done, pairs, elapsed, batch = 0, 0, 0.0, 8
+    while elapsed < target_s and done < w.q_len:
+        rows = np.sort(perm[done:done + batch])
+        q = f64(t["q"][:, rows][:, :, h:h + 1])
+        g = f64(t["dout"][:, rows][:, :, h:h + 1]) if t.get("dout") is not None else np.ones_like(q)
+        t0 = time.perf_counter()
+        oracle.forward(q, k, v, q_pos=qpos_all[rows], causal=w.causal, bias=bias, segment_ids=seg)
+        oracle.backward(q, k, v, g, q_pos=qpos_all[rows], causal=w.causal, bias=bias, segment_ids=seg)
+        elapsed += time.perf_counter() - t0
+        pairs += int(oracle.visible_pairs(qpos_all[rows], w.kv_len, w.causal, seg[:, :] if seg is not None else None))
+        done += len(rows)
+    fl = 14 * w.head_dim * pairs
+    return {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} query rows of head 0 (seeded permutation), each against its full visible key set, "
+                      f"float64 forward+backward; {pairs} visible pairs in {elapsed:.1f} s; "
+                      f"host {platform.processor() or platform.machine()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the ring's K/V exchange across devices is not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import long_context_exact_attn_amd as ra
+    from long_context_exact_attn_amd import metrics as M
+    from long_context_exact_attn_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    if not w.backward and not args.fwd_only:
+        w = W.replace(w, backward=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = W.make(w, device=dev)
+    q, k, v, bias, seg = t["q"], t["k"], t["v"], t["bias"], t["segment_ids"]
+    kw = dict(n_ring=w.n_ring, q_chunk=w.q_chunk, k_chunk=w.k_chunk, causal=w.causal, ring_rank=w.ring_rank)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads, w.q_len), dtype=torch.float32, device=dev)
+    if not args.fwd_only:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty_like(lse)
+    names = ["fwd"] if args.fwd_only else ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        ra.blockwise_attn_fwd(q, k, v, bias, seg, out=out, lse=lse, **kw)
+        mark(1)
+        if args.fwd_only:
+            return
+        ra.blockwise_attn_bwd_preprocess(out, t["dout"], delta=delta)
+        mark(2)
+        ra.blockwise_attn_bwd_dkdv(q, k, v, lse, delta, t["dout"], bias, seg, dk=dk, dv=dv, **kw)
+        mark(3)
+        ra.blockwise_attn_bwd_dq(q, k, v, lse, delta, t["dout"], bias, seg, dq=dq, **kw)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: sum(events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)) / args.steps
+           for i, n in enumerate(names)}
+    ms_step = wall * 1e3 / args.steps
+
+    segn = None if seg is None else seg.cpu().numpy()
+    q_first = int(w.q_positions()[0]) if w.q_len else 0
+    pairs = M.visible_pairs_per_head(q_first, w.q_len, w.kv_len, w.causal, segn)
+    if segn is None:
+        pairs *= w.batch
+    fl = M.flops(pairs, w.head_dim, w.heads)
+    kernel_flops = {"fwd": fl["fwd"], "bwd_dkdv": fl["dkdv"], "bwd_dq": fl["dq"]}
+    total_flops = fl["fwd"] if args.fwd_only else fl["fwd_bwd"]
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    kernels = {}
+    for n in names:
+        entry = {"ms": round(per[n], 4)}
+        if n in kernel_flops:
+            entry["tflops"] = round(kernel_flops[n] / (per[n] * 1e-3) / 1e12, 2)
+            entry["frac_peak"] = round(entry["tflops"] / M.PEAK_BF16_TFLOPS, 4)
+        else:   # the preprocess streams out and dout once and writes delta
+            nbytes = 2 * q.numel() * q.element_size() + lse.numel() * 4
+            entry["gbs"] = round(nbytes / (per[n] * 1e-3) / 1e9, 1)
+        kernels[n] = entry
+    dom = max((n for n in names if n in kernel_flops), key=lambda n: per[n])
+    ach = kernel_flops[dom] / (per[dom] * 1e-3) / 1e12
+    fwd_tflops = fl["fwd"] / (per["fwd"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: one device's share of a {w.kv_len}-token causal context "
+                               f"(ring rank {w.ring_rank} of {w.n_ring}), {w.q_len} local queries, "
+                               f"{w.heads} heads, head_dim {w.head_dim}" if w.ring_rank >= 0 else w.name,
+                   "pass": "fwd" if args.fwd_only else "fwd+bwd",
+                   "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim, "q_len": w.q_len,
+                   "kv_len": w.kv_len, "n_ring": w.n_ring, "ring_rank": w.ring_rank, "causal": w.causal,
+                   "q_chunk": w.q_chunk, "k_chunk": w.k_chunk, "bias": w.bias_len > 0,
+                   "segments": w.segments},
+        "frac_peak": round(value / M.PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "fwd_frac_peak": round(fwd_tflops / M.PEAK_BF16_TFLOPS, 4),
+        "tokens_per_s": round(w.batch * w.q_len / (ms_step * 1e-3), 1),
+        "visible_pairs": pairs * w.heads,
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": M.PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / M.PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

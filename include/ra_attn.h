@@ -1,0 +1,147 @@
+/*
+ * ra_attn.h -- C ABI of the blockwise exact ring-attention library (libra_attn.so).
+ *
+ * What is computed.  Exact softmax attention, organised as ring attention:
+ * each device keeps its block of queries while key/value blocks travel
+ * round a ring of n devices, so that every query block meets every K/V
+ * block and the whole attention map is formed ("手把手拆解RingAttention",
+ * section 1 and its comparison table; section 2 for the neighbour
+ * exchange).  On one GPU the ring is a loop: the query block of ring rank r
+ * takes K/V block (r - s) mod n at step s.  The call mirrors the
+ * ringattention(xq, xk, xv, attention_bias, segment_ids, blockwise_kwargs)
+ * interface of "RingAttention核心功能全解析" (section "快速上手"), whose
+ * blockwise_kwargs carry query_chunk_size, key_chunk_size and
+ * causal_block_size=1 (section "分块注意力计算").
+ *
+ * For query i with global position p_i and key j of the same batch row and
+ * head:
+ *   visible(i,j) = (!causal || j <= p_i) && (segment_ids == NULL || seg[j] == seg[p_i])
+ *   s_ij   = scale * <q_i, k_j> + (bias ? bias[h, j mod bias_len] : 0)
+ *   lse_i  = log sum_{visible j} exp(s_ij)            (natural log; -inf if none)
+ *   out_i  = sum_{visible j} exp(s_ij - lse_i) v_j    (0 if none)
+ * and the backward, given dout, recomputes P from lse (the recompute policy
+ * "nothing_saveable" of the same section):
+ *   Delta_i = <dout_i, out_i>,  dS_ij = P_ij (<dout_i, v_j> - Delta_i)
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i
+ *
+ * Conventions shared by every entry point.
+ *  - Layout.  q, out, dout, dq: [B, Lq, H, D]; k, v, dk, dv: [B, Lk, H, D];
+ *    all row-major and contiguous (the [batch, sequence, heads, head_dim]
+ *    sharding layout of the wmrh.cn page, section "计算与通信重叠").
+ *    lse and delta: float32 [B, H, Lq].  bias: float32 [H, bias_len].
+ *    segment_ids: int32 [B, Lk], indexed by global key position.
+ *  - Pointers are DEVICE pointers, 16-byte aligned; the library keeps none
+ *    after it returns and the caller keeps them alive until the stream has
+ *    passed the work.  stream is a hipStream_t (NULL = the null stream).
+ *  - Ring.  n_ring >= 1 blocks of Lb = Lk / n_ring tokens (Lk must be a
+ *    multiple of n_ring: the ring must close).  ring_rank = -1: q holds all
+ *    n_ring blocks (Lq == Lk) and query block r follows its own ring order;
+ *    ring_rank = r in [0, n_ring): q is block r only (Lq == Lb) and
+ *    p_i = r*Lb + i.  In that mode dk/dv are the contributions of rank r's
+ *    queries to every K/V block (zero where none is visible).
+ *  - Chunks.  q_chunk and k_chunk are query_chunk_size / key_chunk_size:
+ *    each must be >= 1 and divide Lb.  The kernels' own tiles nest inside
+ *    any such chunking and masked keys contribute exact zeros, so results do
+ *    not depend on the chunk sizes at all.
+ *  - causal is 0 or 1 (1 = causal_block_size 1, token granularity, on
+ *    global positions).  Fully masked K/V tiles are skipped.
+ *  - dtype: RA_BF16 (inputs/outputs bfloat16, float32 accumulation, P
+ *    rounded to bfloat16 before the P.V product) or RA_F32 (float32
+ *    throughout).  head_dim must be 64 or 128.
+ *  - Inputs must be finite.
+ *  - Errors.  All validation runs on the host before anything is enqueued;
+ *    a non-zero return means nothing was launched, and ra_last_error()
+ *    describes it.  RA_ERR_HIP reports a failed launch.  Faults during
+ *    execution surface at the caller's next synchronisation.
+ *  - Thread safety.  Entry points keep no state apart from the per-thread
+ *    error string; concurrent calls on different streams are safe.
+ */
+#ifndef RA_ATTN_H
+#define RA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ra_dtype { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+typedef enum ra_status {
+  RA_OK = 0,
+  RA_ERR_ARG = -1,          /* null pointer, causal not 0/1, bad chunk, bad rank */
+  RA_ERR_SHAPE = -2,        /* ring does not close, Lq inconsistent with ring_rank, negative size */
+  RA_ERR_UNSUPPORTED = -3,  /* head_dim or dtype the kernels do not implement */
+  RA_ERR_WORKSPACE = -4,    /* workspace missing or too small */
+  RA_ERR_HIP = -5           /* the HIP runtime refused a launch */
+} ra_status;
+
+/* Problem description shared by all calls (48 bytes, no padding). */
+typedef struct ra_shape {
+  int32_t batch;      /* B >= 0 */
+  int32_t heads;      /* H >= 0 */
+  int32_t head_dim;   /* D: 64 or 128 */
+  int32_t ring_rank;  /* -1: all blocks; r in [0, n_ring): one rank's query block */
+  int64_t q_len;      /* Lq */
+  int64_t kv_len;     /* Lk = n_ring * Lb */
+  int64_t bias_len;   /* bias row length (>= 1 when bias != NULL); key j uses bias[h, j % bias_len] */
+  float scale;        /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+  int32_t dtype;      /* ra_dtype of q, k, v, out, dout, dq, dk, dv */
+} ra_shape;
+
+/*
+ * Forward pass (steps of the ring for one query block, online-softmax merge).
+ * In:  q [B,Lq,H,D], k, v [B,Lk,H,D] (dtype); bias [H,bias_len] float32 or NULL;
+ *      segment_ids [B,Lk] int32 or NULL.
+ * Out: out [B,Lq,H,D] (dtype, written in full); lse [B,H,Lq] float32 (natural log).
+ * Allocates nothing.
+ */
+int ra_blockwise_attn_fwd(const void* q, const void* k, const void* v, const float* bias,
+                          const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                          int32_t causal, void* out, float* lse, const ra_shape* shape, void* stream);
+
+/* Bytes of device workspace ra_blockwise_attn_bwd needs (Delta, float32 [B,H,Lq]), rounded up to 256. */
+size_t ra_blockwise_attn_bwd_workspace_size(const ra_shape* shape);
+
+/*
+ * Backward pass: recomputes P from lse and writes dq, dk, dv (dtype, same
+ * layouts as q, k, v, written in full).  out and lse are the forward's
+ * outputs for the same arguments.  Runs the three phases below in order on
+ * `stream`; workspace (device, >= ra_blockwise_attn_bwd_workspace_size
+ * bytes) holds Delta.
+ */
+int ra_blockwise_attn_bwd(const void* q, const void* k, const void* v, const float* bias,
+                          const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                          int32_t causal, const void* out, const float* lse, const void* dout, void* dq,
+                          void* dk, void* dv, void* workspace, size_t workspace_bytes, const ra_shape* shape,
+                          void* stream);
+
+/* Backward phase 1: delta[b,h,i] = sum_d dout[b,i,h,d] * out[b,i,h,d] (float32 [B,H,Lq]). */
+int ra_blockwise_attn_bwd_preprocess(const void* out, const void* dout, float* delta, const ra_shape* shape,
+                                     void* stream);
+
+/* Backward phase 2: dk, dv for every key, K/V tiles stationary, query blocks in the order the
+ * K/V block meets them on the ring (its own rank first, then r+1, r+2, ...). */
+int ra_blockwise_attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* bias,
+                               const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                               int32_t causal, const float* lse, const float* delta, const void* dout,
+                               void* dk, void* dv, const ra_shape* shape, void* stream);
+
+/* Backward phase 3: dq, query tiles stationary, K/V blocks in ring order (as the forward). */
+int ra_blockwise_attn_bwd_dq(const void* q, const void* k, const void* v, const float* bias,
+                             const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                             int32_t causal, const float* lse, const float* delta, const void* dout, void* dq,
+                             const ra_shape* shape, void* stream);
+
+/* Description of the last error on the calling thread ("" after a success). */
+const char* ra_last_error(void);
+
+/* Library ABI version: 1. */
+int32_t ra_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_ATTN_H */

@@ -1,0 +1,198 @@
+"""ctypes binding of libra_attn.so -- argument marshalling only.
+
+Each function checks the torch tensors it is given (device, dtype, shape,
+contiguity), allocates outputs the caller did not supply, and passes raw
+device pointers and the current HIP stream to the C entry point of the same
+name (include/ra_attn.h).  All arithmetic happens in the HIP kernels; there
+is no CPU path, and a missing library raises RAError.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+RA_F32, RA_BF16 = 0, 1
+_DTYPES = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
+
+
+class RAError(RuntimeError):
+    """A libra_attn call failed; the message carries the library's description."""
+
+    def __init__(self, code, message):
+        super().__init__(f"libra_attn error {code}: {message}")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("ring_rank", ctypes.c_int32), ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64),
+                ("bias_len", ctypes.c_int64), ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+def library_path():
+    return os.environ.get("RA_ATTN_LIB", os.path.join(_HERE, "libra_attn.so"))
+
+
+def load_library():
+    """Load libra_attn.so once; raise RAError if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RAError(-100, f"{path} is missing: build it with long_context_exact_attn_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    SH = ctypes.POINTER(Shape)
+    sig = {
+        "ra_blockwise_attn_fwd": [P, P, P, P, P, I32, I64, I64, I32, P, P, SH, P],
+        "ra_blockwise_attn_bwd": [P, P, P, P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, SZ, SH, P],
+        "ra_blockwise_attn_bwd_preprocess": [P, P, P, SH, P],
+        "ra_blockwise_attn_bwd_dkdv": [P, P, P, P, P, I32, I64, I64, I32, P, P, P, P, P, SH, P],
+        "ra_blockwise_attn_bwd_dq": [P, P, P, P, P, I32, I64, I64, I32, P, P, P, P, SH, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.ra_blockwise_attn_bwd_workspace_size.argtypes = [SH]
+    lib.ra_blockwise_attn_bwd_workspace_size.restype = SZ
+    lib.ra_last_error.argtypes = []
+    lib.ra_last_error.restype = ctypes.c_char_p
+    lib.ra_abi_version.argtypes = []
+    lib.ra_abi_version.restype = ctypes.c_int32
+    if lib.ra_abi_version() != 1:
+        raise RAError(-101, "unexpected libra_attn ABI version")
+    _LIB = lib
+    return lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise RAError(rc, _LIB.ra_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def make_shape(q, k, *, ring_rank=-1, scale=None, bias=None):
+    B, Lq, H, D = q.shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q shape {tuple(q.shape)}")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return Shape(B, H, D, ring_rank, Lq, k.shape[1], 0 if bias is None else bias.shape[-1],
+                 0.0 if scale is None else float(scale), _DTYPES[q.dtype])
+
+
+def _tensors(q, k, v, bias, segment_ids, extra=()):
+    for name, t in (("q", q), ("k", k), ("v", v), *extra):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.dtype != q.dtype or v.dtype != q.dtype or v.shape != k.shape:
+        raise ValueError("k and v must match each other and q's dtype")
+    if bias is not None and (bias.dtype != torch.float32 or bias.dim() != 2 or bias.shape[0] != q.shape[2]
+                             or not bias.is_cuda or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 GPU tensor of shape [heads, bias_len]")
+    if segment_ids is not None and (segment_ids.dtype != torch.int32 or tuple(segment_ids.shape) !=
+                                    (k.shape[0], k.shape[1]) or not segment_ids.is_cuda
+                                    or not segment_ids.is_contiguous()):
+        raise ValueError("segment_ids must be a contiguous int32 GPU tensor of shape [batch, kv_len]")
+
+
+def blockwise_attn_fwd(q, k, v, bias=None, segment_ids=None, *, n_ring, q_chunk, k_chunk, causal,
+                       ring_rank=-1, scale=None, out=None, lse=None):
+    """out, lse = ra_blockwise_attn_fwd(...) on the current stream of q's device."""
+    lib = load_library()
+    _tensors(q, k, v, bias, segment_ids)
+    shape = make_shape(q, k, ring_rank=ring_rank, scale=scale, bias=bias)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    _tensors(q, k, v, None, None, extra=(("out", out), ("lse", lse)))
+    _check(lib.ra_blockwise_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(n_ring),
+                                     int(q_chunk), int(k_chunk), int(bool(causal)), _ptr(out), _ptr(lse),
+                                     ctypes.byref(shape), _stream(q.device)))
+    return out, lse
+
+
+def bwd_workspace_size(q, k, *, ring_rank=-1):
+    lib = load_library()
+    shape = make_shape(q, k, ring_rank=ring_rank)
+    return int(lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(shape)))
+
+
+def blockwise_attn_bwd(q, k, v, out, lse, dout, bias=None, segment_ids=None, *, n_ring, q_chunk, k_chunk,
+                       causal, ring_rank=-1, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """dq, dk, dv = ra_blockwise_attn_bwd(...) on the current stream of q's device."""
+    lib = load_library()
+    _tensors(q, k, v, bias, segment_ids, extra=(("out", out), ("lse", lse), ("dout", dout)))
+    shape = make_shape(q, k, ring_rank=ring_rank, scale=scale, bias=bias)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = int(lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.ra_blockwise_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(n_ring),
+                                     int(q_chunk), int(k_chunk), int(bool(causal)), _ptr(out), _ptr(lse),
+                                     _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), ctypes.byref(shape),
+                                     _stream(q.device)))
+    return dq, dk, dv
+
+
+def blockwise_attn_bwd_preprocess(out, dout, *, delta=None):
+    """delta = ra_blockwise_attn_bwd_preprocess(out, dout): float32 [B, H, Lq]."""
+    lib = load_library()
+    _tensors(out, out, out, None, None, extra=(("dout", dout),))
+    B, Lq, H, D = out.shape
+    shape = Shape(B, H, D, -1, Lq, Lq, 0, 0.0, _DTYPES[out.dtype])
+    if delta is None:
+        delta = torch.empty((B, H, Lq), dtype=torch.float32, device=out.device)
+    _check(lib.ra_blockwise_attn_bwd_preprocess(_ptr(out), _ptr(dout), _ptr(delta), ctypes.byref(shape),
+                                                _stream(out.device)))
+    return delta
+
+
+def blockwise_attn_bwd_dkdv(q, k, v, lse, delta, dout, bias=None, segment_ids=None, *, n_ring, q_chunk,
+                            k_chunk, causal, ring_rank=-1, scale=None, dk=None, dv=None):
+    lib = load_library()
+    _tensors(q, k, v, bias, segment_ids, extra=(("lse", lse), ("delta", delta), ("dout", dout)))
+    shape = make_shape(q, k, ring_rank=ring_rank, scale=scale, bias=bias)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(lib.ra_blockwise_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(n_ring),
+                                          int(q_chunk), int(k_chunk), int(bool(causal)), _ptr(lse), _ptr(delta),
+                                          _ptr(dout), _ptr(dk), _ptr(dv), ctypes.byref(shape), _stream(q.device)))
+    return dk, dv
+
+
+def blockwise_attn_bwd_dq(q, k, v, lse, delta, dout, bias=None, segment_ids=None, *, n_ring, q_chunk, k_chunk,
+                          causal, ring_rank=-1, scale=None, dq=None):
+    lib = load_library()
+    _tensors(q, k, v, bias, segment_ids, extra=(("lse", lse), ("delta", delta), ("dout", dout)))
+    shape = make_shape(q, k, ring_rank=ring_rank, scale=scale, bias=bias)
+    dq = torch.empty_like(q) if dq is None else dq
+    _check(lib.ra_blockwise_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(n_ring),
+                                        int(q_chunk), int(k_chunk), int(bool(causal)), _ptr(lse), _ptr(delta),
+                                        _ptr(dout), _ptr(dq), ctypes.byref(shape), _stream(q.device)))
+    return dq
+
+
+def default_scale(head_dim):
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,366 @@
+// Forward blockwise ring attention, bfloat16 in / float32 accumulate, MFMA on gfx950.
+//
+// One workgroup = 4 wavefronts = one query tile of BQ = 4 * 32 * NQB rows of one
+// (batch, head); the tile stays resident (Q in VGPRs) while the K/V tiles of the
+// ring walk stream through LDS, two buffers deep.  Per K/V tile of BK = 64 keys
+// each wave computes
+//   S^T = K . Q^T           v_mfma_f32_32x32x16_bf16, rows = keys, columns = queries
+//   online-softmax update   every lane owns one query column, so row max / row sum are
+//                           in-lane plus one exchange with lane^32
+//   O^T += V^T . P^T        P^T comes straight from the S^T accumulator registers;
+//                           V^T is read from the row-major LDS tile with ds_read_b64_tr_b16
+// and the epilogue writes out = O / l and lse = m + log l.
+//
+// The merge rule is the online softmax: a running row maximum m (log2 units), a
+// running sum l and an unnormalised accumulator O; a new tile rescales them by
+// exp2(m_old - m_new).  The rescale is deferred while the new maximum exceeds the
+// stored one by at most kTau (P then stays <= 2^kTau), which is exact because O
+// and l always share the same reference m.
+#include "ra_common.cuh"
+
+namespace ra {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int BK = 64;            // keys per K/V tile
+constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
+
+template <int D>
+struct FwdLds {
+  static constexpr int SROW = D + 8;          // padded row stride (bf16 elements), 16-byte multiple
+  static constexpr int TILE = BK * SROW;
+};
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Transposed read: within each 16-lane group, lane j receives element (j % 4) of
+// the 4-element chunks addressed by lanes 4e + j/4 for e = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr(const __bf16* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ float wave_max_pair(float x) {   // max with lane ^ 32
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
+__global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(Params p) {
+  constexpr int QW = 32 * NQB;         // queries per wave
+  constexpr int BQ = kWaves * QW;      // queries per workgroup
+  constexpr int KK = D / 16;           // k-steps of S^T (head_dim / 16)
+  constexpr int DB = D / 32;           // 32-row blocks of O^T
+  constexpr int SROW = FwdLds<D>::SROW;
+  constexpr int TILE = FwdLds<D>::TILE;
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int CPT = BK * CPR / kThreads;   // chunks per thread per tile
+  static_assert(CPT * kThreads == BK * CPR, "tile load must divide evenly");
+
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][TILE];
+  __shared__ float sBias[2][BK];
+  __shared__ int sSeg[2][BK];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- which query tile: heads/batches vary fastest so that consecutive workgroups,
+  // which the dispatcher spreads round-robin over the XCDs, keep one head per XCD
+  // when B*H is a multiple of 8; the heaviest (latest) query tiles go first.
+  const int HB = p.B * p.H;
+  const int64_t n_qt_blk = (p.Lb + BQ - 1) / BQ;
+  const int64_t n_qt = (p.ring_rank < 0 ? p.n_ring : 1) * n_qt_blk;
+  const int64_t wg = blockIdx.x;
+  const int hb = static_cast<int>(wg % HB);
+  const int64_t t = n_qt - 1 - wg / HB;
+  const int b = hb / p.H, h = hb % p.H;
+  const int r_local = static_cast<int>(t / n_qt_blk);
+  const int64_t qa = (t % n_qt_blk) * BQ;                  // first row of the tile inside its block
+  const int r = p.ring_rank < 0 ? r_local : p.ring_rank;
+  const int64_t qrow_base = static_cast<int64_t>(r_local) * p.Lb;   // local row of the block's row 0
+  const int64_t pos0 = static_cast<int64_t>(r) * p.Lb + qa;         // global position of the tile's row 0
+  const int64_t nrows = (p.Lb - qa) < BQ ? (p.Lb - qa) : BQ;
+
+  const __bf16* __restrict__ qp = static_cast<const __bf16*>(p.q);
+  const __bf16* __restrict__ kp = static_cast<const __bf16*>(p.k);
+  const __bf16* __restrict__ vp = static_cast<const __bf16*>(p.v);
+
+  // ---- the wave's queries, as the B operand of S^T = K . Q^T
+  const int64_t wrow0 = qa + wave * QW;                      // first row of the wave inside the block
+  const int64_t wpos0 = pos0 + wave * QW;
+  const int64_t wvalid = p.Lb - wrow0;                       // rows of this wave that exist (may be <= 0)
+  bf16x8 Qf[NQB][KK];
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) {
+    const int64_t row = wrow0 + nb * 32 + l32;
+    const bool ok = row < p.Lb;
+    const __bf16* src = qp + row_offset(b, qrow_base + (ok ? row : 0), h, p.Lq, p.H, D);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      bf16x8 x = *reinterpret_cast<const bf16x8*>(src + 16 * kk + 8 * hh);
+      Qf[nb][kk] = ok ? x : bf16x8{};
+    }
+  }
+  int qseg[NQB];
+  if constexpr (HAS_SEG) {
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+      int64_t pos = wpos0 + nb * 32 + l32;
+      qseg[nb] = (wrow0 + nb * 32 + l32 < p.Lb) ? p.seg[static_cast<int64_t>(b) * p.Lk + pos] : 0;
+    }
+  }
+
+  const float c = p.scale * kLog2e;   // raw score -> log2 units
+  float m[NQB], lsum[NQB];
+  f32x16 O[DB][NQB];
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) {
+    m[nb] = -INFINITY;
+    lsum[nb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) O[db][nb] = f32x16{};
+  }
+
+  // ---- K/V tile staging: global -> registers -> LDS (two buffers)
+  uint4 kreg[CPT], vreg[CPT];
+  float breg = 0.f;
+  int sreg = 0;
+  auto load_tile = [&](int64_t key0, int64_t kend) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cidx = tid + i * kThreads;
+      const int row = cidx / CPR;
+      const int col = (cidx % CPR) * 8;
+      const int64_t key = key0 + row;
+      if (key < kend) {
+        const int64_t off = row_offset(b, key, h, p.Lk, p.H, D) + col;
+        kreg[i] = *reinterpret_cast<const uint4*>(kp + off);
+        vreg[i] = *reinterpret_cast<const uint4*>(vp + off);
+      } else {
+        kreg[i] = uint4{0, 0, 0, 0};
+        vreg[i] = uint4{0, 0, 0, 0};
+      }
+    }
+    if (tid < BK) {
+      const int64_t key = key0 + tid;
+      if constexpr (HAS_BIAS)
+        breg = key < kend ? p.bias[static_cast<int64_t>(h) * p.bias_len + key % p.bias_len] * kLog2e : 0.f;
+      if constexpr (HAS_SEG) sreg = key < kend ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cidx = tid + i * kThreads;
+      const int row = cidx / CPR;
+      const int col = (cidx % CPR) * 8;
+      *reinterpret_cast<uint4*>(&sK[buf][row * SROW + col]) = kreg[i];
+      *reinterpret_cast<uint4*>(&sV[buf][row * SROW + col]) = vreg[i];
+    }
+    if (tid < BK) {
+      if constexpr (HAS_BIAS) sBias[buf][tid] = breg;
+      if constexpr (HAS_SEG) sSeg[buf][tid] = sreg;
+    }
+  };
+
+  RingWalk walk;
+  walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
+  bool have = nrows > 0 && walk.next<BK>();
+  int buf = 0;
+  int64_t key0 = 0, kend = 0;
+  if (have) {
+    key0 = walk.key0;
+    kend = walk.kend;
+    load_tile(key0, kend);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  while (have) {
+    const bool more = walk.next<BK>();
+    const int64_t nkey0 = walk.key0, nkend = walk.kend;
+    if (more) load_tile(nkey0, nkend);   // in flight while this tile is computed
+
+    const __bf16* Kt = sK[buf];
+    const __bf16* Vt = sV[buf];
+    const bool wave_active = wvalid > 0 && !(CAUSAL && key0 > wpos0 + (wvalid < QW ? wvalid : QW) - 1);
+    if (wave_active) {
+      // ---- S^T = K . Q^T : rows = 64 keys (two 32-row blocks), columns = the wave's queries
+      f32x16 S[2][NQB];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NQB; ++nb) S[mb][nb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const bf16x8 a = lds_read_b128(Kt + (mb * 32 + l32) * SROW + 16 * kk + 8 * hh);
+#pragma unroll
+          for (int nb = 0; nb < NQB; ++nb)
+            S[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Qf[nb][kk], S[mb][nb], 0, 0, 0);
+        }
+      }
+
+      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > wpos0);
+      bf16x8 P[NQB][2][2];   // [query block][key block][16-key step]
+#pragma unroll
+      for (int nb = 0; nb < NQB; ++nb) {
+        const int64_t qpos = wpos0 + nb * 32 + l32;
+        // logits in log2 units when there is a bias (else raw scores, scaled inside the exp)
+        if constexpr (HAS_BIAS) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int kr = mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+              S[mb][nb][v] = __builtin_fmaf(S[mb][nb][v], c, sBias[buf][kr]);
+            }
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int kr = mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+              const int64_t key = key0 + kr;
+              bool vis = key < kend;
+              if constexpr (CAUSAL) vis = vis && key <= qpos;
+              if constexpr (HAS_SEG) vis = vis && sSeg[buf][kr] == qseg[nb];
+              if (!vis) S[mb][nb][v] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[mb][nb][v]);
+        mx = wave_max_pair(mx);
+        const float mxs = HAS_BIAS ? mx : mx * c;
+        // Each row decides for itself whether its maximum grew by more than kTau; the
+        // multiply runs only when some row of the wave needs it, with alpha = 1 (exact)
+        // for the others, so a row's result never depends on its neighbours' data.
+        const bool grow = mxs > m[nb] + kTau;
+        if (__ballot(grow) != 0) {
+          const float mnew = grow ? mxs : m[nb];
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m[nb] - mnew) : 1.f;   // m = -inf gives 0
+          lsum[nb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) O[db][nb] *= alpha;
+          m[nb] = mnew;
+        }
+        const float msub = (m[nb] == -INFINITY) ? 0.f : m[nb];
+        float rs = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            float e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float x = S[mb][nb][8 * st + i];
+              e[i] = HAS_BIAS ? __builtin_amdgcn_exp2f(x - msub) : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -msub));
+              rs += e[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bf16x2 pr = __builtin_convertvector((f32x2){e[2 * i], e[2 * i + 1]}, bf16x2);
+              P[nb][mb][st][2 * i] = pr[0];
+              P[nb][mb][st][2 * i + 1] = pr[1];
+            }
+          }
+        lsum[nb] += rs;
+      }
+
+      // ---- O^T += V^T . P^T ; V^T operand through transposed LDS reads
+      const int g = lane >> 4, gi = lane & 15;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int rbase = mb * 32 + st * 16 + 4 * hh + (gi >> 2);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
+            const i16x4 lo = lds_read_tr(Vt + rbase * SROW + col);
+            const i16x4 hi = lds_read_tr(Vt + (rbase + 8) * SROW + col);
+            bf16x8 a;
+            __builtin_memcpy(&a, &lo, 8);
+            __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
+#pragma unroll
+            for (int nb = 0; nb < NQB; ++nb)
+              O[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[nb][mb][st], O[db][nb], 0, 0, 0);
+          }
+        }
+    }
+
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    key0 = nkey0;
+    kend = nkend;
+    have = more;
+  }
+
+  // ---- epilogue: out = O / l, lse = m + log l (natural log)
+  __bf16* __restrict__ op = static_cast<__bf16*>(p.out);
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) {
+    const int64_t row = wrow0 + nb * 32 + l32;
+    const float lt = lsum[nb] + __shfl_xor(lsum[nb], 32);
+    if (row >= p.Lb || row < 0) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    __bf16* dst = op + row_offset(b, qrow_base + row, h, p.Lq, p.H, D);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        bf16x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = (__bf16)(O[db][nb][4 * v4 + i] * inv);
+        *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * v4 + 4 * hh) = o4;
+      }
+    if (hh == 0)
+      p.lse[(static_cast<int64_t>(b) * p.H + h) * p.Lq + qrow_base + row] =
+          lt > 0.f ? (m[nb] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
+hipError_t launch_t(const Params& p, hipStream_t st) {
+  constexpr int BQ = kWaves * 32 * NQB;
+  const int64_t n_qt = (p.ring_rank < 0 ? p.n_ring : 1) * ((p.Lb + BQ - 1) / BQ);
+  const int64_t grid = n_qt * p.B * p.H;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, NQB, CAUSAL, HAS_BIAS, HAS_SEG>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int D, int NQB>
+hipError_t launch_d(const Params& p, hipStream_t st) {
+  const bool c = p.causal != 0, bi = p.bias != nullptr, sg = p.seg != nullptr;
+  if (c) {
+    if (bi) return sg ? launch_t<D, NQB, true, true, true>(p, st) : launch_t<D, NQB, true, true, false>(p, st);
+    return sg ? launch_t<D, NQB, true, false, true>(p, st) : launch_t<D, NQB, true, false, false>(p, st);
+  }
+  if (bi) return sg ? launch_t<D, NQB, false, true, true>(p, st) : launch_t<D, NQB, false, true, false>(p, st);
+  return sg ? launch_t<D, NQB, false, false, true>(p, st) : launch_t<D, NQB, false, false, false>(p, st);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_mfma(const Params& p, hipStream_t st) {
+  if (p.D == 64) return launch_d<64, 2>(p, st);
+  if (p.D == 128) return launch_d<128, 1>(p, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ra

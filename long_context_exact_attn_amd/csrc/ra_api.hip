@@ -1,0 +1,284 @@
+// C ABI of libra_attn: argument validation on the host, then kernel dispatch.
+// The operations are defined in include/ra_attn.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/ra_attn.h"
+#include "ra_common.cuh"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return RA_OK;
+}
+
+#define RA_TRY(x)              \
+  do {                         \
+    const int rc_ = (x);       \
+    if (rc_ != RA_OK) return rc_; \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Checked {
+  ra::Params p;
+  int64_t q_elems, kv_elems, rows;   // rows = B*H*Lq
+};
+
+// dtype, head_dim and sign checks.
+int check_dims(const ra_shape* s) {
+  if (!s) return fail(RA_ERR_ARG, "shape is NULL");
+  if (s->dtype != RA_F32 && s->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "dtype %d is not RA_F32 or RA_BF16", s->dtype);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", s->head_dim);
+  if (s->batch < 0 || s->heads < 0 || s->q_len < 0 || s->kv_len < 0)
+    return fail(RA_ERR_SHAPE, "negative size (batch %d, heads %d, q_len %lld, kv_len %lld)", s->batch, s->heads,
+                (long long)s->q_len, (long long)s->kv_len);
+  return RA_OK;
+}
+
+// Shape-level checks shared by every entry point that walks the ring.
+int check_shape(const ra_shape* s, int32_t n_ring, Checked* c) {
+  RA_TRY(check_dims(s));
+  if (n_ring < 1) return fail(RA_ERR_ARG, "n_ring must be >= 1 (got %d)", n_ring);
+  if (s->kv_len % n_ring != 0)
+    return fail(RA_ERR_SHAPE, "ring does not close: kv_len %lld is not a multiple of n_ring %d", (long long)s->kv_len,
+                n_ring);
+  const int64_t Lb = s->kv_len / n_ring;
+  if (s->ring_rank < -1 || s->ring_rank >= n_ring)
+    return fail(RA_ERR_ARG, "ring_rank %d outside [-1, %d)", s->ring_rank, n_ring);
+  if (s->ring_rank < 0 && s->q_len != s->kv_len)
+    return fail(RA_ERR_SHAPE, "ring_rank -1 needs q_len == kv_len (got %lld and %lld)", (long long)s->q_len,
+                (long long)s->kv_len);
+  if (s->ring_rank >= 0 && s->q_len != Lb)
+    return fail(RA_ERR_SHAPE, "ring_rank %d needs q_len == kv_len / n_ring = %lld (got %lld)", s->ring_rank,
+                (long long)Lb, (long long)s->q_len);
+  if (std::isnan(s->scale)) return fail(RA_ERR_ARG, "scale is NaN");
+  const int64_t HB = static_cast<int64_t>(s->batch) * s->heads;
+  if (HB > (int64_t(1) << 30)) return fail(RA_ERR_SHAPE, "batch*heads too large");
+  ra::Params& p = c->p;
+  p = ra::Params{};
+  p.Lq = s->q_len;
+  p.Lk = s->kv_len;
+  p.Lb = Lb;
+  p.bias_len = s->bias_len;
+  p.B = s->batch;
+  p.H = s->heads;
+  p.D = s->head_dim;
+  p.n_ring = n_ring;
+  p.ring_rank = s->ring_rank;
+  p.bf16 = s->dtype == RA_BF16;
+  p.scale = s->scale > 0.f ? s->scale : 1.0f / std::sqrt(static_cast<float>(s->head_dim));
+  c->q_elems = HB * s->q_len * s->head_dim;
+  c->kv_elems = HB * s->kv_len * s->head_dim;
+  c->rows = HB * s->q_len;
+  // every grid used is at most (query or key tiles of 64) x B x H workgroups
+  const int64_t tiles = (Lb + 63) / 64 * (s->ring_rank < 0 ? n_ring : 1);
+  const int64_t ktiles = (Lb + 63) / 64 * n_ring;
+  if ((tiles > ktiles ? tiles : ktiles) * HB > 0x7fffffffLL) return fail(RA_ERR_SHAPE, "problem too large for one launch");
+  return RA_OK;
+}
+
+int check_mask_args(const ra_shape* s, const float* bias, int64_t q_chunk, int64_t k_chunk, int32_t causal,
+                    Checked* c) {
+  const int64_t Lb = c->p.Lb;
+  if (causal != 0 && causal != 1) return fail(RA_ERR_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (q_chunk < 1 || k_chunk < 1) return fail(RA_ERR_ARG, "q_chunk and k_chunk must be >= 1");
+  if (Lb > 0 && (Lb % q_chunk != 0 || Lb % k_chunk != 0))
+    return fail(RA_ERR_ARG, "q_chunk %lld and k_chunk %lld must divide the ring block length %lld",
+                (long long)q_chunk, (long long)k_chunk, (long long)Lb);
+  if (bias && s->bias_len < 1) return fail(RA_ERR_ARG, "bias given with bias_len %lld", (long long)s->bias_len);
+  c->p.causal = causal;
+  if (!bias) c->p.bias_len = 1;
+  return RA_OK;
+}
+
+int need_ptr(const void* ptr, int64_t elems, const char* name, size_t align) {
+  if (elems == 0) return RA_OK;
+  if (!ptr) return fail(RA_ERR_ARG, "%s is NULL", name);
+  if (!aligned(ptr, align)) return fail(RA_ERR_ARG, "%s is not %zu-byte aligned", name, align);
+  return RA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_inputs(const Checked& c, const void* q, const void* k, const void* v, const float* bias,
+                 const int32_t* seg, const ra_shape* s) {
+  RA_TRY(need_ptr(q, c.q_elems, "q", 16));
+  RA_TRY(need_ptr(k, c.kv_elems, "k", 16));
+  RA_TRY(need_ptr(v, c.kv_elems, "v", 16));
+  if (bias && !aligned(bias, 4)) return fail(RA_ERR_ARG, "bias is not 4-byte aligned");
+  if (seg && !aligned(seg, 4)) return fail(RA_ERR_ARG, "segment_ids is not 4-byte aligned");
+  (void)s;
+  return RA_OK;
+}
+
+size_t workspace_bytes(const Checked& c) {
+  const size_t b = static_cast<size_t>(c.rows) * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
+int do_bwd_dkdv(const Checked& c, hipStream_t st) {
+  return hip_status(ra::launch_bwd_dkdv_simt(c.p, st), "dK/dV launch");
+}
+
+int do_bwd_dq(const Checked& c, hipStream_t st) {
+  return hip_status(ra::launch_bwd_dq_simt(c.p, st), "dQ launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ra_abi_version(void) { return 1; }
+
+const char* ra_last_error(void) { return g_last_error.c_str(); }
+
+int ra_blockwise_attn_fwd(const void* q, const void* k, const void* v, const float* bias,
+                          const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                          int32_t causal, void* out, float* lse, const ra_shape* shape, void* stream) {
+  Checked c;
+  RA_TRY(check_shape(shape, n_ring, &c));
+  RA_TRY(check_mask_args(shape, bias, q_chunk, k_chunk, causal, &c));
+  RA_TRY(check_inputs(c, q, k, v, bias, segment_ids, shape));
+  RA_TRY(need_ptr(out, c.q_elems, "out", 16));
+  RA_TRY(need_ptr(lse, c.rows, "lse", 4));
+  if (c.rows == 0) return ok();
+  c.p.q = q;
+  c.p.k = k;
+  c.p.v = v;
+  c.p.bias = bias;
+  c.p.seg = segment_ids;
+  c.p.out = out;
+  c.p.lse = lse;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (c.p.bf16) return hip_status(ra::launch_fwd_mfma(c.p, st), "forward launch");
+  return hip_status(ra::launch_fwd_simt(c.p, st), "forward launch");
+}
+
+size_t ra_blockwise_attn_bwd_workspace_size(const ra_shape* shape) {
+  if (!shape || shape->batch < 0 || shape->heads < 0 || shape->q_len < 0) return 0;
+  const size_t rows = static_cast<size_t>(shape->batch) * shape->heads * shape->q_len;
+  return (rows * sizeof(float) + 255) / 256 * 256;
+}
+
+int ra_blockwise_attn_bwd_preprocess(const void* out, const void* dout, float* delta, const ra_shape* shape,
+                                     void* stream) {
+  RA_TRY(check_dims(shape));
+  Checked c;
+  c.p = ra::Params{};
+  c.p.B = shape->batch;
+  c.p.H = shape->heads;
+  c.p.D = shape->head_dim;
+  c.p.Lq = shape->q_len;
+  c.p.bf16 = shape->dtype == RA_BF16;
+  c.rows = static_cast<int64_t>(shape->batch) * shape->heads * shape->q_len;
+  c.q_elems = c.rows * shape->head_dim;
+  if ((c.rows + 255) / 256 > 0x7fffffffLL) return fail(RA_ERR_SHAPE, "problem too large for one launch");
+  RA_TRY(need_ptr(out, c.q_elems, "out", 16));
+  RA_TRY(need_ptr(dout, c.q_elems, "dout", 16));
+  RA_TRY(need_ptr(delta, c.rows, "delta", 4));
+  if (c.rows == 0) return ok();
+  c.p.out = const_cast<void*>(out);
+  c.p.dout = dout;
+  c.p.delta_out = delta;
+  return hip_status(ra::launch_bwd_preprocess(c.p, static_cast<hipStream_t>(stream)), "preprocess launch");
+}
+
+static int bwd_common(const void* q, const void* k, const void* v, const float* bias, const int32_t* seg,
+                      int32_t n_ring, int64_t q_chunk, int64_t k_chunk, int32_t causal, const float* lse,
+                      const void* dout, const ra_shape* shape, Checked* c) {
+  RA_TRY(check_shape(shape, n_ring, c));
+  RA_TRY(check_mask_args(shape, bias, q_chunk, k_chunk, causal, c));
+  RA_TRY(check_inputs(*c, q, k, v, bias, seg, shape));
+  RA_TRY(need_ptr(lse, c->rows, "lse", 4));
+  RA_TRY(need_ptr(dout, c->q_elems, "dout", 16));
+  c->p.q = q;
+  c->p.k = k;
+  c->p.v = v;
+  c->p.bias = bias;
+  c->p.seg = seg;
+  c->p.lse = const_cast<float*>(lse);
+  c->p.dout = dout;
+  return RA_OK;
+}
+
+int ra_blockwise_attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* bias,
+                               const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                               int32_t causal, const float* lse, const float* delta, const void* dout,
+                               void* dk, void* dv, const ra_shape* shape, void* stream) {
+  Checked c;
+  RA_TRY(bwd_common(q, k, v, bias, segment_ids, n_ring, q_chunk, k_chunk, causal, lse, dout, shape, &c));
+  RA_TRY(need_ptr(delta, c.rows, "delta", 4));
+  RA_TRY(need_ptr(dk, c.kv_elems, "dk", 16));
+  RA_TRY(need_ptr(dv, c.kv_elems, "dv", 16));
+  if (c.kv_elems == 0) return ok();
+  c.p.delta = delta;
+  c.p.dk = dk;
+  c.p.dv = dv;
+  return do_bwd_dkdv(c, static_cast<hipStream_t>(stream));
+}
+
+int ra_blockwise_attn_bwd_dq(const void* q, const void* k, const void* v, const float* bias,
+                             const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                             int32_t causal, const float* lse, const float* delta, const void* dout, void* dq,
+                             const ra_shape* shape, void* stream) {
+  Checked c;
+  RA_TRY(bwd_common(q, k, v, bias, segment_ids, n_ring, q_chunk, k_chunk, causal, lse, dout, shape, &c));
+  RA_TRY(need_ptr(delta, c.rows, "delta", 4));
+  RA_TRY(need_ptr(dq, c.q_elems, "dq", 16));
+  if (c.rows == 0) return ok();
+  c.p.delta = delta;
+  c.p.dq = dq;
+  return do_bwd_dq(c, static_cast<hipStream_t>(stream));
+}
+
+int ra_blockwise_attn_bwd(const void* q, const void* k, const void* v, const float* bias,
+                          const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                          int32_t causal, const void* out, const float* lse, const void* dout, void* dq,
+                          void* dk, void* dv, void* workspace, size_t workspace_bytes_given,
+                          const ra_shape* shape, void* stream) {
+  Checked c;
+  RA_TRY(bwd_common(q, k, v, bias, segment_ids, n_ring, q_chunk, k_chunk, causal, lse, dout, shape, &c));
+  RA_TRY(need_ptr(out, c.q_elems, "out", 16));
+  RA_TRY(need_ptr(dq, c.q_elems, "dq", 16));
+  RA_TRY(need_ptr(dk, c.kv_elems, "dk", 16));
+  RA_TRY(need_ptr(dv, c.kv_elems, "dv", 16));
+  const size_t need = workspace_bytes(c);
+  if (need > 0 && (!workspace || workspace_bytes_given < need))
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes_given,
+                workspace ? "" : " (NULL)");
+  if (workspace && !aligned(workspace, 4)) return fail(RA_ERR_WORKSPACE, "workspace is not 4-byte aligned");
+  if (c.kv_elems == 0 && c.q_elems == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  c.p.out = const_cast<void*>(out);
+  c.p.delta_out = static_cast<float*>(workspace);
+  c.p.delta = static_cast<const float*>(workspace);
+  c.p.dq = dq;
+  c.p.dk = dk;
+  c.p.dv = dv;
+  if (c.rows > 0) RA_TRY(hip_status(ra::launch_bwd_preprocess(c.p, st), "preprocess launch"));
+  if (c.kv_elems > 0) RA_TRY(do_bwd_dkdv(c, st));
+  if (c.rows > 0) RA_TRY(do_bwd_dq(c, st));
+  return ok();
+}
+
+}  // extern "C"

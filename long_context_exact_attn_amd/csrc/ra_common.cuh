@@ -1,0 +1,144 @@
+// Internal definitions shared by the kernels and the C-ABI layer of libra_attn.
+//
+// Ring schedule (the one fact every kernel shares): the query block of ring
+// rank r meets K/V block (r - s) mod n at ring step s, because each device
+// keeps its queries while key/value blocks move one device round the ring per
+// step ("手把手拆解RingAttention", section 1; section 2 for the exchange).
+// Under a causal mask K/V blocks past the query block are invisible and are
+// skipped without being read; inside the diagonal block only keys up to the
+// tile's last query are visited.  In the backward pass a K/V block meets
+// the query blocks in the opposite direction: ranks j, j+1, ... (mod n).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Everything a kernel needs; filled by the C-ABI layer after validation.
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* bias;        // [H, bias_len] or null
+  const int32_t* seg;       // [B, Lk] or null
+  void* out;                // [B, Lq, H, D]
+  float* lse;               // [B, H, Lq]
+  const void* dout;         // [B, Lq, H, D]
+  const float* delta;       // [B, H, Lq]
+  float* delta_out;         // preprocess output
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t Lq, Lk, Lb, bias_len;
+  int32_t B, H, D, n_ring, ring_rank, causal;
+  int32_t bf16;             // 1: bfloat16 tensors, 0: float32
+  float scale;              // resolved (> 0)
+};
+
+// ---------------------------------------------------------------- element access
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ int64_t row_offset(int b, int64_t row, int h, int64_t L, int H, int D) {
+  return ((static_cast<int64_t>(b) * L + row) * H + h) * static_cast<int64_t>(D);
+}
+
+// ---------------------------------------------------------------- forward-direction ring walk
+// Walks the K/V tiles one query tile must visit, in ring order, tile size BK.
+// Start with begin(); each next() moves to the following tile and returns
+// false when the walk is over.  key0 is the tile's first global key; kend is
+// the end of its K/V block (keys at or past kend are padding of a ragged
+// tile and must be treated as invisible).
+struct RingWalk {
+  int n, r, s;
+  bool causal;
+  int64_t Lb, plast;  // plast: last global query position of the tile
+  int64_t key0, kend, kstop;
+  __device__ void begin(int n_, int r_, int64_t Lb_, bool causal_, int64_t plast_) {
+    n = n_; r = r_; Lb = Lb_; causal = causal_; plast = plast_;
+    s = -1; key0 = 0; kend = 0; kstop = 0;
+  }
+  template <int BK>
+  __device__ bool next() {
+    key0 += BK;
+    while (key0 >= kstop) {
+      ++s;
+      if (s >= n) return false;
+      int j = r - s;
+      if (j < 0) j += n;
+      if (causal && j > r) continue;   // a block from the future: fully masked, skipped
+      key0 = static_cast<int64_t>(j) * Lb;
+      kend = key0 + Lb;
+      kstop = (causal && j == r) ? (plast + 1 < kend ? plast + 1 : kend) : kend;
+    }
+    return true;
+  }
+};
+
+// ---------------------------------------------------------------- backward-direction ring walk
+// Walks the query tiles one K/V tile must meet: the K/V block j visits ranks
+// j, j+1, ... (mod n).  With ring_rank >= 0 only that rank's queries exist.
+// Under a causal mask ranks before j are skipped and, in rank j itself, query
+// tiles that end before the K/V tile's first key are skipped.
+struct QueryWalk {
+  int n, j, s, rank_only;
+  bool causal;
+  int64_t Lb, kfirst;   // kfirst: first global key of the K/V tile
+  int64_t row0, rend, rstop;   // local query rows [row0, row0+BQ) of q; rend: end of the rank's rows
+  int64_t pos_base;            // global position of local row 0 of the current rank
+  int cur_rank;
+  __device__ void begin(int n_, int j_, int64_t Lb_, bool causal_, int64_t kfirst_, int rank_only_) {
+    n = n_; j = j_; Lb = Lb_; causal = causal_; kfirst = kfirst_; rank_only = rank_only_;
+    s = -1; row0 = 0; rend = 0; rstop = 0; pos_base = 0; cur_rank = 0;
+  }
+  template <int BQ>
+  __device__ bool next() {
+    row0 += BQ;
+    while (row0 >= rstop) {
+      ++s;
+      if (s >= n) return false;
+      int r = j + s;
+      if (r >= n) r -= n;
+      if (rank_only >= 0 && r != rank_only) continue;
+      if (causal && r < j) continue;        // queries before the block see none of it
+      cur_rank = r;
+      int64_t local0 = rank_only >= 0 ? 0 : static_cast<int64_t>(r) * Lb;   // first local row of rank r
+      pos_base = static_cast<int64_t>(r) * Lb - local0;                       // global pos = local row + pos_base
+      rend = local0 + Lb;
+      row0 = local0;
+      if (causal && r == j) {
+        // skip whole query tiles that end before kfirst: first row with pos >= kfirst
+        int64_t first_row = kfirst - pos_base;
+        if (first_row > row0) row0 += ((first_row - row0) / BQ) * BQ;
+      }
+      rstop = rend;
+    }
+    return true;
+  }
+};
+
+// ---------------------------------------------------------------- launchers (validated Params only)
+hipError_t launch_fwd_mfma(const Params& p, hipStream_t st);
+hipError_t launch_fwd_simt(const Params& p, hipStream_t st);
+hipError_t launch_bwd_preprocess(const Params& p, hipStream_t st);
+hipError_t launch_bwd_dkdv_simt(const Params& p, hipStream_t st);
+hipError_t launch_bwd_dq_simt(const Params& p, hipStream_t st);
+hipError_t launch_bwd_dkdv_mfma(const Params& p, hipStream_t st);
+hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t st);
+
+}  // namespace ra

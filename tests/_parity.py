@@ -1,0 +1,95 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C-ABI
+binding, run the oracle on the same (rounded) inputs, and compare."""
+import numpy as np
+import torch
+
+import long_context_exact_attn_amd as ra
+import oracle
+from long_context_exact_attn_amd import workloads as W
+
+# tolerances: float32 path max abs 1e-4 on outputs; bfloat16 path max abs 2e-2 and
+# relative RMS 1e-2 on outputs and gradients; lse (float32 in both) max abs 1e-3 / 1e-5
+TOL = {"f32": dict(max_abs=1e-4, rel_rms=None, lse=1e-5), "bf16": dict(max_abs=2e-2, rel_rms=1e-2, lse=1e-3)}
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def gpu_forward(w, t, **over):
+    kw = dict(n_ring=w.n_ring, q_chunk=w.q_chunk, k_chunk=w.k_chunk, causal=w.causal, ring_rank=w.ring_rank)
+    kw.update(over)
+    return ra.blockwise_attn_fwd(t["q"], t["k"], t["v"], t["bias"], t["segment_ids"], **kw)
+
+
+def gpu_backward(w, t, out, lse, **over):
+    kw = dict(n_ring=w.n_ring, q_chunk=w.q_chunk, k_chunk=w.k_chunk, causal=w.causal, ring_rank=w.ring_rank)
+    kw.update(over)
+    return ra.blockwise_attn_bwd(t["q"], t["k"], t["v"], out, lse, t["dout"], t["bias"], t["segment_ids"], **kw)
+
+
+def oracle_inputs(t, heads=None, rows=None):
+    """float64 numpy copies of the inputs, optionally for some heads / query rows."""
+    hs = slice(None) if heads is None else heads
+    q = t["q"][:, :, hs]
+    if rows is not None:
+        q = q[:, rows]
+    d = dict(q=np64(q), k=np64(t["k"][:, :, hs]), v=np64(t["v"][:, :, hs]),
+             bias=None if t["bias"] is None else np64(t["bias"][hs]),
+             segment_ids=None if t["segment_ids"] is None else t["segment_ids"].cpu().numpy())
+    if t.get("dout") is not None:
+        g = t["dout"][:, :, hs]
+        d["dout"] = np64(g if rows is None else g[:, rows])
+    return d
+
+
+def oracle_forward(w, d, q_pos):
+    return oracle.forward(d["q"], d["k"], d["v"], q_pos=q_pos, causal=w.causal, bias=d["bias"],
+                          segment_ids=d["segment_ids"])
+
+
+def errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = got - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff) / nref) if nref > 0 else float(np.linalg.norm(diff))
+    return max_abs, rel
+
+
+def assert_close(name, got, ref, dtype):
+    tol = TOL[dtype]
+    max_abs, rel = errors(got, ref)
+    msg = f"{name}: max_abs={max_abs:.3e} rel_rms={rel:.3e}"
+    print(msg, flush=True)
+    assert np.all(np.isfinite(got)), name + ": non-finite values"
+    assert max_abs <= tol["max_abs"], msg
+    if tol["rel_rms"] is not None:
+        assert rel <= tol["rel_rms"], msg
+
+
+def assert_lse(got, ref, dtype):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    same_inf = np.isneginf(got) == np.isneginf(ref)
+    assert np.all(same_inf), "lse: rows with no visible key differ"
+    fin = np.isfinite(ref)
+    err = float(np.max(np.abs(got[fin] - ref[fin]))) if fin.any() else 0.0
+    print(f"lse: max_abs={err:.3e}", flush=True)
+    assert err <= TOL[dtype]["lse"], f"lse max_abs {err}"
+
+
+def sample_rows(w, n, seed=0):
+    """A fixed sample of local query rows: n seeded rows plus the first and last row of every ring block
+    the queries span."""
+    rng = np.random.default_rng(seed)
+    Lq, Lb = w.q_len, w.block_len
+    rows = set(rng.choice(Lq, size=min(n, Lq), replace=False).tolist())
+    for start in range(0, Lq, Lb):
+        rows.update((start, start + Lb - 1))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def make(w, device):
+    return W.make(w, device=device)

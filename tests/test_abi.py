@@ -1,0 +1,145 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every symbol the
+header declares, and rejects bad arguments before anything is launched.
+
+Every rejected call below also leaves at least one required output pointer
+NULL, so that a validation bug could never reach a kernel launch with the
+fake (non-dereferenceable) input pointers these tests use.  The call-based
+tests are skipped where a GPU is visible; they belong to the CPU suite.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_exact_attn_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra_attn.h")
+
+FAKE = ctypes.c_void_p(0x7f0000010000)   # aligned, never dereferenced: every call below fails validation
+
+
+def _lib():
+    try:
+        return api.load_library()
+    except api.RAError as e:
+        pytest.fail(f"library not built: {e}")
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib()
+    names = _declared_functions()
+    assert "ra_blockwise_attn_fwd" in names and "ra_blockwise_attn_bwd" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.ra_abi_version() == 1
+
+
+def test_shape_struct_layout():
+    assert ctypes.sizeof(api.Shape) == 48
+    assert api.Shape.q_len.offset == 16 and api.Shape.scale.offset == 40 and api.Shape.dtype.offset == 44
+
+
+def test_workspace_size():
+    lib = _lib()
+    s = api.Shape(2, 3, 64, -1, 1000, 1000, 0, 0.0, api.RA_BF16)
+    assert lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(s)) == (2 * 3 * 1000 * 4 + 255) // 256 * 256
+    s = api.Shape(0, 3, 64, -1, 0, 0, 0, 0.0, api.RA_BF16)
+    assert lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(s)) == 0
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+needs_cpu = pytest.mark.skipif(_gpu_visible(), reason="validation calls with fake pointers run on the CPU suite only")
+
+
+def _fwd(lib, shape, n_ring=4, q_chunk=64, k_chunk=64, causal=1, out=None, lse=None, bias=None, seg=None,
+         q=FAKE, k=FAKE, v=FAKE):
+    return lib.ra_blockwise_attn_fwd(q, k, v, bias, seg, n_ring, q_chunk, k_chunk, causal, out, lse,
+                                     ctypes.byref(shape) if shape is not None else None, None)
+
+
+@needs_cpu
+@pytest.mark.parametrize("case,expect", [
+    ("ring_not_closed", -2), ("rank_out_of_range", -1), ("q_len_vs_rank", -2), ("all_ranks_q_len", -2),
+    ("head_dim", -3), ("dtype", -3), ("negative", -2), ("causal", -1), ("chunk_zero", -1),
+    ("chunk_not_dividing", -1), ("n_ring_zero", -1), ("bias_len", -1), ("null_out", -1), ("null_lse", -1),
+    ("null_q", -1), ("misaligned_k", -1), ("null_shape", -1),
+])
+def test_forward_validation(case, expect):
+    lib = _lib()
+    S = lambda **kw: api.Shape(**{**dict(batch=1, heads=2, head_dim=64, ring_rank=-1, q_len=1024, kv_len=1024,  # noqa
+                                         bias_len=0, scale=0.0, dtype=api.RA_BF16), **kw})
+    kw = {}
+    shape = S()
+    if case == "ring_not_closed":
+        kw["n_ring"] = 3
+    elif case == "rank_out_of_range":
+        shape = S(ring_rank=4, q_len=256)
+    elif case == "q_len_vs_rank":
+        shape = S(ring_rank=1, q_len=1024)
+    elif case == "all_ranks_q_len":
+        shape = S(q_len=512)
+    elif case == "head_dim":
+        shape = S(head_dim=96)
+    elif case == "dtype":
+        shape = S(dtype=7)
+    elif case == "negative":
+        shape = S(batch=-1)
+    elif case == "causal":
+        kw["causal"] = 2
+    elif case == "chunk_zero":
+        kw["q_chunk"] = 0
+    elif case == "chunk_not_dividing":
+        kw["k_chunk"] = 100
+    elif case == "n_ring_zero":
+        kw["n_ring"] = 0
+    elif case == "bias_len":
+        kw["bias"] = FAKE
+    elif case == "null_lse":
+        kw["out"] = FAKE
+    elif case == "null_q":
+        kw["q"] = None
+    elif case == "misaligned_k":
+        kw["k"] = ctypes.c_void_p(0x7f0000010008)
+    elif case == "null_shape":
+        shape = None
+    rc = _fwd(lib, shape, **kw)
+    assert rc == expect, (case, rc, lib.ra_last_error())
+    assert lib.ra_last_error()
+
+
+@needs_cpu
+def test_backward_validation():
+    lib = _lib()
+    s = api.Shape(1, 2, 64, -1, 1024, 1024, 0, 0.0, api.RA_BF16)
+    # workspace missing: every tensor pointer is given, dv is NULL so the call cannot launch regardless
+    rc = lib.ra_blockwise_attn_bwd(FAKE, FAKE, FAKE, None, None, 4, 256, 256, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None, None, 0, ctypes.byref(s), None)
+    assert rc == -1 and "dv" in lib.ra_last_error().decode()
+    rc = lib.ra_blockwise_attn_bwd_dkdv(FAKE, FAKE, FAKE, None, None, 5, 256, 256, 1, FAKE, FAKE, FAKE, FAKE, None,
+                                        ctypes.byref(s), None)
+    assert rc == -2
+    rc = lib.ra_blockwise_attn_bwd_dq(FAKE, FAKE, FAKE, None, None, 4, 256, 256, 1, FAKE, None, FAKE, FAKE,
+                                      ctypes.byref(s), None)
+    assert rc == -1 and "delta" in lib.ra_last_error().decode()
+    s2 = api.Shape(1, 2, 48, -1, 1024, 1024, 0, 0.0, api.RA_BF16)
+    rc = lib.ra_blockwise_attn_bwd_preprocess(FAKE, FAKE, None, ctypes.byref(s2), None)
+    assert rc == -3
+
+
+@needs_cpu
+def test_empty_problem_is_a_no_op():
+    lib = _lib()
+    s = api.Shape(0, 2, 64, -1, 1024, 1024, 0, 0.0, api.RA_BF16)   # batch 0: nothing to do, NULLs allowed
+    assert _fwd(lib, s, q=None, k=None, v=None) == 0
+    assert lib.ra_last_error() == b""

@@ -1,0 +1,189 @@
+"""GPU parity: the HIP path (through the C-ABI) against the float64 CPU oracle
+on the same seeded inputs, plus properties that must hold at any size."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_exact_attn_amd as ra
+from long_context_exact_attn_amd import workloads as W
+import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_forward(w, dev, rows=None, heads=None):
+    t = P.make(w, dev)
+    out, lse = P.gpu_forward(w, t)
+    torch.cuda.synchronize()
+    qpos = w.q_positions()
+    sel = slice(None) if rows is None else rows
+    d = P.oracle_inputs(t, heads=heads, rows=rows)
+    ref_o, ref_l = P.oracle_forward(w, d, qpos[sel])
+    hs = slice(None) if heads is None else heads
+    got_o = P.np64(out[:, :, hs][:, sel])
+    got_l = lse[:, hs].detach().cpu().numpy().astype(np.float64)[:, :, sel]
+    P.assert_close(f"{w.name} out", got_o, ref_o, w.dtype)
+    P.assert_lse(got_l, ref_l, w.dtype)
+    return t, out, lse
+
+
+# ------------------------------------------------------------------ the configured workloads
+def test_tiny_f32_full(gpu):
+    w = W.WORKLOADS["tiny-f32-1k"]
+    t, out, lse = _check_forward(w, gpu)
+    # all segment ids 0 means no masking: identical to passing no segment ids at all
+    out2, lse2 = ra.blockwise_attn_fwd(t["q"], t["k"], t["v"], None, None, n_ring=w.n_ring, q_chunk=w.q_chunk,
+                                       k_chunk=w.k_chunk, causal=w.causal)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_causal_32k_sampled_rows(gpu):
+    w = W.WORKLOADS["causal-32k"]
+    _check_forward(w, gpu, rows=P.sample_rows(w, 512, seed=1))
+
+
+def test_share_1m_rank7_sampled_rows(gpu):
+    w = W.WORKLOADS["share-1m-r7"]
+    _check_forward(w, gpu, rows=P.sample_rows(w, 96, seed=2), heads=slice(0, 16, 5))
+
+
+def test_packed_docs_64k_sampled_rows(gpu):
+    w = W.WORKLOADS["packed-docs-64k"]
+    _check_forward(w, gpu, rows=P.sample_rows(w, 192, seed=3), heads=slice(0, 32, 7))
+
+
+def test_train_32k_one_head_full_backward(gpu):
+    w = W.WORKLOADS["train-32k"]
+    t = P.make(w, gpu)
+    out, lse = P.gpu_forward(w, t)
+    dq, dk, dv = P.gpu_backward(w, t, out, lse)
+    torch.cuda.synchronize()
+    h = 3
+    d = P.oracle_inputs(t, heads=slice(h, h + 1))
+    import oracle
+    rdq, rdk, rdv, _ = oracle.backward(d["q"], d["k"], d["v"], d["dout"], q_pos=w.q_positions(), causal=True)
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        P.assert_close(f"{w.name} {name}[h={h}]", P.np64(g[:, :, h:h + 1]), r, "bf16")
+    # invariants on every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i
+    sdk = dk.float().sum(dim=1)
+    sdv, sdo = dv.float().sum(dim=1), t["dout"].float().sum(dim=1)
+    scale_k = dk.float().abs().sum(dim=1)
+    assert torch.all(sdk.abs() <= 2e-2 * scale_k + 1e-3), float((sdk.abs() / scale_k).max())
+    assert torch.allclose(sdv, sdo, rtol=2e-2, atol=2e-1), float((sdv - sdo).abs().max())
+
+
+# ------------------------------------------------------------------ small full-tensor sweep
+SWEEP = [
+    # (name, kwargs)
+    ("causal-ring4", dict(kv_len=1024, n_ring=4)),
+    ("noncausal-ring2", dict(kv_len=512, n_ring=2, causal=False)),
+    ("rank0", dict(kv_len=2048, n_ring=4, ring_rank=0)),
+    ("rank3", dict(kv_len=2048, n_ring=4, ring_rank=3)),
+    ("rank2-noncausal", dict(kv_len=1536, n_ring=3, ring_rank=2, causal=False)),
+    ("ragged-100", dict(kv_len=400, n_ring=4)),
+    ("ragged-250-rank1", dict(kv_len=1000, n_ring=4, ring_rank=1)),
+    ("ragged-1-token-blocks", dict(kv_len=7, n_ring=7)),
+    ("bias", dict(kv_len=1024, n_ring=2, bias_len=300)),
+    ("segments", dict(kv_len=1024, n_ring=4, segments="docs", doc_len=(20, 200))),
+    ("bias-seg-noncausal", dict(kv_len=768, n_ring=3, causal=False, bias_len=64, segments="docs", doc_len=(5, 90))),
+    ("d128", dict(head_dim=128, kv_len=1024, n_ring=4, heads=3)),
+    ("d128-all", dict(head_dim=128, kv_len=960, n_ring=3, batch=2, bias_len=100, segments="docs", doc_len=(30, 300),
+                      ring_rank=2)),
+    ("batch3-heads5", dict(batch=3, heads=5, kv_len=640, n_ring=5)),
+    ("n_ring1", dict(kv_len=1000, n_ring=1)),
+    ("f32-causal-seg", dict(dtype="f32", kv_len=600, n_ring=3, segments="docs", doc_len=(10, 150), bias_len=33)),
+    ("f32-d128-rank1", dict(dtype="f32", head_dim=128, kv_len=512, n_ring=4, ring_rank=1)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SWEEP, ids=[s[0] for s in SWEEP])
+def test_small_forward(gpu, name, kw):
+    w = W.small(name, **kw)
+    _check_forward(w, gpu)
+
+
+@pytest.mark.parametrize("name,kw", [s for s in SWEEP if s[0] not in ("ragged-1-token-blocks",)],
+                         ids=[s[0] for s in SWEEP if s[0] not in ("ragged-1-token-blocks",)])
+def test_small_backward(gpu, name, kw):
+    w = W.small(name, backward=True, **kw)
+    t = P.make(w, gpu)
+    out, lse = P.gpu_forward(w, t)
+    dq, dk, dv = P.gpu_backward(w, t, out, lse)
+    torch.cuda.synchronize()
+    d = P.oracle_inputs(t)
+    import oracle
+    rdq, rdk, rdv, _ = oracle.backward(d["q"], d["k"], d["v"], d["dout"], q_pos=w.q_positions(), causal=w.causal,
+                                       bias=d["bias"], segment_ids=d["segment_ids"])
+    tol = "f32" if w.dtype == "f32" else "bf16"
+    if tol == "f32":
+        # float32 gradients accumulate over many keys; allow 1e-4 relative to the gradient's scale
+        for name_, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            err = np.max(np.abs(P.np64(g) - r))
+            print(f"{name_}: max_abs={err:.3e}", flush=True)
+            assert err <= 1e-4 * max(1.0, np.max(np.abs(r)))
+    else:
+        for name_, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            P.assert_close(name_, P.np64(g), r, "bf16")
+
+
+# ------------------------------------------------------------------ properties
+def test_chunk_sizes_do_not_change_results(gpu):
+    w = W.small("chunks", kv_len=2048, n_ring=2, bias_len=128, segments="docs", doc_len=(50, 400))
+    t = P.make(w, gpu)
+    ref = P.gpu_forward(w, t, q_chunk=1024, k_chunk=1024)
+    for qc, kc in ((1, 1), (64, 512), (256, 8), (1024, 16)):
+        o, l_ = P.gpu_forward(w, t, q_chunk=qc, k_chunk=kc)
+        assert torch.equal(o, ref[0]) and torch.equal(l_, ref[1]), (qc, kc)
+
+
+def test_ring_order_changes_only_rounding(gpu):
+    base = W.small("ring", kv_len=4096, n_ring=1, heads=4)
+    t = P.make(base, gpu)
+    o1, l1 = P.gpu_forward(base, t)
+    for n in (2, 4, 8, 16):
+        o, l_ = P.gpu_forward(base, t, n_ring=n, q_chunk=4096 // n, k_chunk=4096 // n)
+        P.assert_close(f"n_ring={n} vs 1", P.np64(o), P.np64(o1), "bf16")
+        assert float((l_ - l1).abs().max()) < 1e-4
+
+
+def test_masked_keys_do_not_leak(gpu):
+    # causal: rewriting every key/value after position p leaves rows <= p bitwise unchanged
+    w = W.small("leak", kv_len=2048, n_ring=4, heads=2, segments="docs", doc_len=(40, 300), bias_len=512)
+    t = P.make(w, gpu)
+    o1, l1 = P.gpu_forward(w, t)
+    p = 1234
+    t2 = dict(t)
+    t2["k"] = t["k"].clone()
+    t2["v"] = t["v"].clone()
+    t2["k"][:, p + 1:] = torch.randn_like(t["k"][:, p + 1:].float()).to(t["k"].dtype) * 3
+    t2["v"][:, p + 1:] = torch.randn_like(t["v"][:, p + 1:].float()).to(t["v"].dtype) * 3
+    o2, l2 = P.gpu_forward(w, t2)
+    assert torch.equal(o1[:, :p + 1], o2[:, :p + 1]) and torch.equal(l1[:, :, :p + 1], l2[:, :, :p + 1])
+    assert not torch.equal(o1[:, p + 1:], o2[:, p + 1:])
+
+
+def test_forward_is_deterministic(gpu):
+    w = W.small("det", kv_len=4096, n_ring=8, heads=4, bias_len=100)
+    t = P.make(w, gpu)
+    o1, l1 = P.gpu_forward(w, t)
+    for _ in range(3):
+        o, l_ = P.gpu_forward(w, t)
+        assert torch.equal(o, o1) and torch.equal(l_, l1)
+
+
+def test_empty_inputs(gpu):
+    q = torch.empty(0, 256, 2, 64, dtype=torch.bfloat16, device=gpu)
+    out, lse = ra.blockwise_attn_fwd(q, q, q, n_ring=1, q_chunk=256, k_chunk=256, causal=True)
+    assert out.shape == q.shape and lse.shape == (0, 2, 256)
+    q = torch.empty(1, 0, 2, 64, dtype=torch.bfloat16, device=gpu)
+    out, lse = ra.blockwise_attn_fwd(q, q, q, n_ring=4, q_chunk=1, k_chunk=1, causal=True)
+    assert out.shape == q.shape
+
+
+def test_errors_surface_as_exceptions(gpu):
+    q = torch.zeros(1, 1000, 2, 64, dtype=torch.bfloat16, device=gpu)
+    with pytest.raises(ra.RAError, match="ring does not close"):
+        ra.blockwise_attn_fwd(q, q, q, n_ring=3, q_chunk=1, k_chunk=1, causal=True)
+    q96 = torch.zeros(1, 64, 2, 96, dtype=torch.bfloat16, device=gpu)
+    with pytest.raises(ra.RAError, match="head_dim"):
+        ra.blockwise_attn_fwd(q96, q96, q96, n_ring=1, q_chunk=64, k_chunk=64, causal=True)
