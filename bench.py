@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--fwd-only", action="store_true", help="time the forward alone (not the bench line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the steps, run one plain device copy of this many MiB (a known-size kernel "
+                         "that calibrates the profiler's HBM byte counters)")
     return ap.parse_args()
 
 
@@ -117,6 +120,13 @@ def main():
         ra.blockwise_attn_bwd_dq(q, k, v, lse, delta, t["dout"], bias, seg, dq=dq, **kw)
         mark(4)
 
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written", file=sys.stderr)
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
