@@ -1,0 +1,601 @@
+// Backward blockwise ring attention, bfloat16 in / float32 accumulate, MFMA on gfx950.
+//
+// The probabilities are recomputed from the saved logsumexp, P = exp(s - lse),
+// so no score matrix is ever stored (the recompute policy of the pages'
+// blockwise_kwargs).  Two kernels, each owning the rows it writes, so the
+// result is deterministic and needs no atomics:
+//
+// dK/dV kernel -- one workgroup owns BKW keys of one (batch, head): each wave
+//   keeps 32 * NKB keys' K and V rows in VGPRs and walks the query tiles that
+//   K/V block meets on the ring (its own rank first, then the later ones);
+//   query tiles (Q, dO, lse, Delta, segment ids) stream through LDS, two
+//   buffers deep.  Per query tile and 32-query block:
+//     S  = Q . K^T,  dP = dO . V^T     (rows = queries, columns = the lane's key)
+//     P  = exp2(S * scale * log2e + bias - lse * log2e),  dS = P (dP - Delta)
+//     dV^T += dO^T . P,  dK^T += Q^T . dS     (dO^T, Q^T by transposing LDS reads)
+// dQ kernel -- the forward's tiling: one workgroup owns a query tile (Q, dO,
+//   lse, Delta in VGPRs) and K/V tiles stream through LDS in ring order:
+//     S^T = K . Q^T,  dP^T = V . dO^T,  dS^T as above,  dQ^T += K^T . dS^T
+#include "mfma_util.cuh"
+
+namespace ra {
+namespace {
+
+// ================================================================== dQ (query tiles stationary)
+constexpr int kBkDq = 64;   // keys per K/V tile
+
+template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
+__global__ __launch_bounds__(kThreads) void dq_mfma_kernel(Params p) {
+  constexpr int BK = kBkDq;
+  constexpr int QW = 32 * NQB;         // queries per wave
+  constexpr int BQ = kWaves * QW;      // queries per workgroup
+  constexpr int KK = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int SROW = D + 8;
+  constexpr int TILE = BK * SROW;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = BK * CPR / kThreads;
+  static_assert(CPT * kThreads == BK * CPR, "tile load must divide evenly");
+
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][TILE];
+  __shared__ float sBias[2][BK];
+  __shared__ __attribute__((aligned(16))) int sSeg[2][BK];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // tile order as in the forward: heads fastest, heaviest query tiles first
+  const int HB = p.B * p.H;
+  const int64_t n_qt_blk = (p.Lb + BQ - 1) / BQ;
+  const int64_t n_qt = (p.ring_rank < 0 ? p.n_ring : 1) * n_qt_blk;
+  const int64_t wg = blockIdx.x;
+  const int hb = static_cast<int>(wg % HB);
+  const int64_t t = n_qt - 1 - wg / HB;
+  const int b = hb / p.H, h = hb % p.H;
+  const int r_local = static_cast<int>(t / n_qt_blk);
+  const int64_t qa = (t % n_qt_blk) * BQ;
+  const int r = p.ring_rank < 0 ? r_local : p.ring_rank;
+  const int64_t qrow_base = static_cast<int64_t>(r_local) * p.Lb;
+  const int64_t pos0 = static_cast<int64_t>(r) * p.Lb + qa;
+  const int64_t nrows = (p.Lb - qa) < BQ ? (p.Lb - qa) : BQ;
+
+  const __bf16* __restrict__ qp = static_cast<const __bf16*>(p.q);
+  const __bf16* __restrict__ kp = static_cast<const __bf16*>(p.k);
+  const __bf16* __restrict__ vp = static_cast<const __bf16*>(p.v);
+  const __bf16* __restrict__ gp = static_cast<const __bf16*>(p.dout);
+
+  const int64_t wrow0 = qa + wave * QW;
+  const int64_t wpos0 = pos0 + wave * QW;
+  const int64_t wvalid = p.Lb - wrow0;
+  bf16x8 Qf[NQB][KK], Gf[NQB][KK];
+  float lse2[NQB], dlt[NQB];
+  int qseg[NQB];
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) {
+    const int64_t row = wrow0 + nb * 32 + l32;
+    const bool ok = row < p.Lb;
+    const int64_t off = row_offset(b, qrow_base + (ok ? row : 0), h, p.Lq, p.H, D);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + off + 16 * kk + 8 * hh);
+      const bf16x8 y = *reinterpret_cast<const bf16x8*>(gp + off + 16 * kk + 8 * hh);
+      Qf[nb][kk] = ok ? x : bf16x8{};
+      Gf[nb][kk] = ok ? y : bf16x8{};
+    }
+    const int64_t li = (static_cast<int64_t>(b) * p.H + h) * p.Lq + qrow_base + (ok ? row : 0);
+    const float L = p.lse[li];
+    // rows that do not exist or see no key get P = 0 everywhere (exp2(-inf))
+    lse2[nb] = (ok && L != -INFINITY) ? L * kLog2e : INFINITY;
+    dlt[nb] = ok ? p.delta[li] : 0.f;
+    qseg[nb] = (HAS_SEG && ok) ? p.seg[static_cast<int64_t>(b) * p.Lk + wpos0 + nb * 32 + l32] : 0;
+  }
+
+  const float c = p.scale * kLog2e;
+  f32x16 dQ[DB][NQB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) dQ[db][nb] = f32x16{};
+
+  uint4 kreg[CPT], vreg[CPT];
+  float breg = 0.f;
+  int sreg = 0;
+  auto load_tile = [&](int64_t key0, int64_t kend) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cidx = tid + i * kThreads;
+      const int row = cidx / CPR;
+      const int col = (cidx % CPR) * 8;
+      const int64_t key = key0 + row;
+      if (key < kend) {
+        const int64_t off = row_offset(b, key, h, p.Lk, p.H, D) + col;
+        kreg[i] = *reinterpret_cast<const uint4*>(kp + off);
+        vreg[i] = *reinterpret_cast<const uint4*>(vp + off);
+      } else {
+        kreg[i] = uint4{0, 0, 0, 0};
+        vreg[i] = uint4{0, 0, 0, 0};
+      }
+    }
+    if (tid < BK) {
+      const int64_t key = key0 + tid;
+      if constexpr (HAS_BIAS)
+        breg = key < kend ? p.bias[static_cast<int64_t>(h) * p.bias_len + key % p.bias_len] * kLog2e : 0.f;
+      if constexpr (HAS_SEG) sreg = key < kend ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cidx = tid + i * kThreads;
+      const int row = cidx / CPR;
+      const int col = (cidx % CPR) * 8;
+      *reinterpret_cast<uint4*>(&sK[buf][row * SROW + col]) = kreg[i];
+      *reinterpret_cast<uint4*>(&sV[buf][row * SROW + col]) = vreg[i];
+    }
+    if (tid < BK) {
+      if constexpr (HAS_BIAS) sBias[buf][tid] = breg;
+      if constexpr (HAS_SEG) sSeg[buf][tid] = sreg;
+    }
+  };
+
+  RingWalk walk;
+  walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
+  bool have = nrows > 0 && walk.next<BK>();
+  int buf = 0;
+  int64_t key0 = 0, kend = 0;
+  if (have) {
+    key0 = walk.key0;
+    kend = walk.kend;
+    load_tile(key0, kend);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  while (have) {
+    const bool more = walk.next<BK>();
+    const int64_t nkey0 = walk.key0, nkend = walk.kend;
+    if (more) load_tile(nkey0, nkend);
+
+    const __bf16* Kt = sK[buf];
+    const __bf16* Vt = sV[buf];
+    const bool wave_active = wvalid > 0 && !(CAUSAL && key0 > wpos0 + (wvalid < QW ? wvalid : QW) - 1);
+    if (wave_active) {
+      f32x16 S[2][NQB], G[2][NQB];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NQB; ++nb) {
+          S[mb][nb] = f32x16{};
+          G[mb][nb] = f32x16{};
+        }
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const bf16x8 ak = lds_read_b128(Kt + (mb * 32 + l32) * SROW + 16 * kk + 8 * hh);
+          const bf16x8 av = lds_read_b128(Vt + (mb * 32 + l32) * SROW + 16 * kk + 8 * hh);
+#pragma unroll
+          for (int nb = 0; nb < NQB; ++nb) {
+            S[mb][nb] = mfma32(ak, Qf[nb][kk], S[mb][nb]);
+            G[mb][nb] = mfma32(av, Gf[nb][kk], G[mb][nb]);
+          }
+        }
+      }
+
+      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > wpos0);
+      int kseg[2][16];
+      if constexpr (HAS_SEG) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int4 x = *reinterpret_cast<const int4*>(&sSeg[buf][mb * 32 + 8 * g4 + 4 * hh]);
+            kseg[mb][4 * g4 + 0] = x.x;
+            kseg[mb][4 * g4 + 1] = x.y;
+            kseg[mb][4 * g4 + 2] = x.z;
+            kseg[mb][4 * g4 + 3] = x.w;
+          }
+      }
+      bf16x8 dS[NQB][2][2];
+#pragma unroll
+      for (int nb = 0; nb < NQB; ++nb) {
+        // key kr of the tile is visible to this lane's query iff kr <= klim and (segments) ids match
+        int klim = BK - 1;
+        if (need_mask) {
+          klim = static_cast<int>((kend - key0) < BK ? (kend - key0) : BK) - 1;
+          if constexpr (CAUSAL) {
+            const int64_t rel = wpos0 + nb * 32 + l32 - key0;
+            klim = rel < klim ? static_cast<int>(rel < -1 ? -1 : rel) : klim;
+          }
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            float e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int v = 8 * st + i;
+              const int kr = mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+              float y = HAS_BIAS ? __builtin_fmaf(S[mb][nb][v], c, sBias[buf][kr] - lse2[nb])
+                                 : __builtin_fmaf(S[mb][nb][v], c, -lse2[nb]);
+              if (need_mask) {
+                bool vis = kr <= klim;
+                if constexpr (HAS_SEG) vis = vis && kseg[mb][v] == qseg[nb];
+                y = vis ? y : -INFINITY;
+              }
+              const float pr = __builtin_amdgcn_exp2f(y);
+              e[i] = pr * (G[mb][nb][v] - dlt[nb]);
+            }
+            dS[nb][mb][st] = pack_bf16x8(e);
+          }
+      }
+
+      // dQ^T += K^T . dS^T
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 a = lds_read_a_transposed<SROW>(Kt, mb * 32, st, db * 32, lane);
+#pragma unroll
+            for (int nb = 0; nb < NQB; ++nb) dQ[db][nb] = mfma32(a, dS[nb][mb][st], dQ[db][nb]);
+          }
+    }
+
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    key0 = nkey0;
+    kend = nkend;
+    have = more;
+  }
+
+  __bf16* __restrict__ dqp = static_cast<__bf16*>(p.dq);
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) {
+    const int64_t row = wrow0 + nb * 32 + l32;
+    if (row >= p.Lb) continue;
+    __bf16* dst = dqp + row_offset(b, qrow_base + row, h, p.Lq, p.H, D);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        bf16x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = (__bf16)(dQ[db][nb][4 * v4 + i] * p.scale);
+        *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * v4 + 4 * hh) = o4;
+      }
+  }
+}
+
+// ================================================================== dK/dV (K/V tiles stationary)
+constexpr int kBqKv = 64;   // queries per LDS tile
+
+template <int D, int NKB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
+__global__ __launch_bounds__(kThreads) void dkdv_mfma_kernel(Params p) {
+  constexpr int BQ = kBqKv;
+  constexpr int KW = 32 * NKB;         // keys per wave
+  constexpr int BKW = kWaves * KW;     // keys per workgroup
+  constexpr int KK = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int SROW = D + 8;
+  constexpr int TILE = BQ * SROW;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = BQ * CPR / kThreads;
+  static_assert(CPT * kThreads == BQ * CPR, "tile load must divide evenly");
+  static_assert(BQ == 64, "two 32-query blocks per tile");
+
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sG[2][TILE];
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];    // -lse * log2e (-inf: row contributes nothing)
+  __shared__ __attribute__((aligned(16))) float sDl[2][BQ];   // Delta
+  __shared__ __attribute__((aligned(16))) int sSg[2][BQ];     // segment id of the query
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // heads fastest (one head per XCD group, as in the forward); key tiles of block 0 first,
+  // which under a causal mask meet the most query blocks
+  const int HB = p.B * p.H;
+  const int64_t n_kt_blk = (p.Lb + BKW - 1) / BKW;
+  const int64_t wg = blockIdx.x;
+  const int hb = static_cast<int>(wg % HB);
+  const int64_t kt = wg / HB;
+  const int b = hb / p.H, h = hb % p.H;
+  const int j = static_cast<int>(kt / n_kt_blk);
+  const int64_t ka = (kt % n_kt_blk) * BKW;                     // first key of the tile inside block j
+  const int64_t kfirst = static_cast<int64_t>(j) * p.Lb + ka;   // its global position
+  const int64_t wk0 = ka + wave * KW;                           // the wave's first key inside block j
+  const int64_t wkey0 = kfirst + wave * KW;                     // ... and its global position
+
+  const __bf16* __restrict__ qp = static_cast<const __bf16*>(p.q);
+  const __bf16* __restrict__ kp = static_cast<const __bf16*>(p.k);
+  const __bf16* __restrict__ vp = static_cast<const __bf16*>(p.v);
+  const __bf16* __restrict__ gp = static_cast<const __bf16*>(p.dout);
+
+  // the wave's keys, as B operands of S = Q . K^T and dP = dO . V^T
+  bf16x8 Kf[NKB][KK], Vf[NKB][KK];
+  float kbias[NKB];
+  int ksg[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int64_t krow = wk0 + kb * 32 + l32;
+    const bool ok = krow < p.Lb;
+    const int64_t key = static_cast<int64_t>(j) * p.Lb + (ok ? krow : 0);
+    const int64_t off = row_offset(b, key, h, p.Lk, p.H, D);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(kp + off + 16 * kk + 8 * hh);
+      const bf16x8 y = *reinterpret_cast<const bf16x8*>(vp + off + 16 * kk + 8 * hh);
+      Kf[kb][kk] = ok ? x : bf16x8{};
+      Vf[kb][kk] = ok ? y : bf16x8{};
+    }
+    kbias[kb] = (HAS_BIAS && ok) ? p.bias[static_cast<int64_t>(h) * p.bias_len + key % p.bias_len] * kLog2e : 0.f;
+    ksg[kb] = (HAS_SEG && ok) ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
+  }
+
+  const float c = p.scale * kLog2e;
+  f32x16 dK[DB][NKB], dV[DB][NKB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      dK[db][kb] = f32x16{};
+      dV[db][kb] = f32x16{};
+    }
+
+  // ---- query tile staging: global -> registers -> LDS (two buffers)
+  uint4 qreg[CPT], greg[CPT];
+  float lreg = 0.f, dreg = 0.f;
+  int sreg = 0;
+  auto load_tile = [&](int64_t row0, int64_t rend, int64_t pbase) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cidx = tid + i * kThreads;
+      const int row = cidx / CPR;
+      const int col = (cidx % CPR) * 8;
+      const int64_t r = row0 + row;
+      if (r < rend) {
+        const int64_t off = row_offset(b, r, h, p.Lq, p.H, D) + col;
+        qreg[i] = *reinterpret_cast<const uint4*>(qp + off);
+        greg[i] = *reinterpret_cast<const uint4*>(gp + off);
+      } else {
+        qreg[i] = uint4{0, 0, 0, 0};
+        greg[i] = uint4{0, 0, 0, 0};
+      }
+    }
+    if (tid < BQ) {
+      const int64_t r = row0 + tid;
+      const bool ok = r < rend;
+      const int64_t li = (static_cast<int64_t>(b) * p.H + h) * p.Lq + (ok ? r : 0);
+      const float L = p.lse[li];
+      lreg = (ok && L != -INFINITY) ? -L * kLog2e : -INFINITY;
+      dreg = ok ? p.delta[li] : 0.f;
+      if constexpr (HAS_SEG) sreg = ok ? p.seg[static_cast<int64_t>(b) * p.Lk + pbase + r] : 0;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cidx = tid + i * kThreads;
+      const int row = cidx / CPR;
+      const int col = (cidx % CPR) * 8;
+      *reinterpret_cast<uint4*>(&sQ[buf][row * SROW + col]) = qreg[i];
+      *reinterpret_cast<uint4*>(&sG[buf][row * SROW + col]) = greg[i];
+    }
+    if (tid < BQ) {
+      sL[buf][tid] = lreg;
+      sDl[buf][tid] = dreg;
+      if constexpr (HAS_SEG) sSg[buf][tid] = sreg;
+    }
+  };
+
+  QueryWalk walk;
+  walk.begin(p.n_ring, j, p.Lb, CAUSAL, kfirst, p.ring_rank);
+  bool have = walk.next<BQ>();
+  int buf = 0;
+  int64_t row0 = 0, rend = 0, pbase = 0;
+  if (have) {
+    row0 = walk.row0;
+    rend = walk.rend;
+    pbase = walk.pos_base;
+    load_tile(row0, rend, pbase);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  while (have) {
+    const bool more = walk.next<BQ>();
+    const int64_t nrow0 = walk.row0, nrend = walk.rend, npbase = walk.pos_base;
+    if (more) load_tile(nrow0, nrend, npbase);
+
+    const __bf16* Qt = sQ[buf];
+    const __bf16* Gt = sG[buf];
+    const int64_t qpos0 = row0 + pbase;                      // global position of the tile's row 0
+    const int64_t nq = (rend - row0) < BQ ? (rend - row0) : BQ;
+    const bool wave_active = wk0 < p.Lb && !(CAUSAL && qpos0 + nq - 1 < wkey0);
+    if (wave_active) {
+      // rows past the rank's end carry -inf in sL, so their P is 0 and only the causal and
+      // segment masks need the selects
+      const bool need_mask = HAS_SEG || (CAUSAL && wkey0 + KW - 1 > qpos0);
+      int krel[NKB];   // the lane's key relative to the tile's row 0, clamped to [0, BQ]
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int64_t rel = wkey0 + kb * 32 + l32 - qpos0;
+        krel[kb] = rel < 0 ? 0 : (rel > BQ ? BQ : static_cast<int>(rel));
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 S[NKB], G[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          S[kb] = f32x16{};
+          G[kb] = f32x16{};
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 aq = lds_read_b128(Qt + (qb * 32 + l32) * SROW + 16 * kk + 8 * hh);
+          const bf16x8 ag = lds_read_b128(Gt + (qb * 32 + l32) * SROW + 16 * kk + 8 * hh);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            S[kb] = mfma32(aq, Kf[kb][kk], S[kb]);
+            G[kb] = mfma32(ag, Vf[kb][kk], G[kb]);
+          }
+        }
+        // the 16 query rows this lane holds: qr(v) = qb*32 + 8*(v/4) + 4*hh + v%4
+        float nl[16], dl[16];
+        int qs[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int base = qb * 32 + 8 * g4 + 4 * hh;
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sL[buf][base]);
+          const f32x4 y = *reinterpret_cast<const f32x4*>(&sDl[buf][base]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            nl[4 * g4 + i] = x[i];
+            dl[4 * g4 + i] = y[i];
+          }
+          if constexpr (HAS_SEG) {
+            const int4 z = *reinterpret_cast<const int4*>(&sSg[buf][base]);
+            qs[4 * g4 + 0] = z.x;
+            qs[4 * g4 + 1] = z.y;
+            qs[4 * g4 + 2] = z.z;
+            qs[4 * g4 + 3] = z.w;
+          }
+        }
+        bf16x8 Pb[NKB][2], Sb[NKB][2];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            float pe[8], de[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int v = 8 * st + i;
+              const int qr = qb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+              float y = HAS_BIAS ? __builtin_fmaf(S[kb][v], c, kbias[kb] + nl[v]) : __builtin_fmaf(S[kb][v], c, nl[v]);
+              if (need_mask) {
+                bool vis = true;
+                if constexpr (CAUSAL) vis = krel[kb] <= qr;
+                if constexpr (HAS_SEG) vis = vis && ksg[kb] == qs[v];
+                y = vis ? y : -INFINITY;
+              }
+              const float pr = __builtin_amdgcn_exp2f(y);
+              pe[i] = pr;
+              de[i] = pr * (G[kb][v] - dl[v]);
+            }
+            Pb[kb][st] = pack_bf16x8(pe);
+            Sb[kb][st] = pack_bf16x8(de);
+          }
+        // dV^T += dO^T . P ;  dK^T += Q^T . dS
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 ag = lds_read_a_transposed<SROW>(Gt, qb * 32, st, db * 32, lane);
+            const bf16x8 aq = lds_read_a_transposed<SROW>(Qt, qb * 32, st, db * 32, lane);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+              dV[db][kb] = mfma32(ag, Pb[kb][st], dV[db][kb]);
+              dK[db][kb] = mfma32(aq, Sb[kb][st], dK[db][kb]);
+            }
+          }
+      }
+    }
+
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    row0 = nrow0;
+    rend = nrend;
+    pbase = npbase;
+    have = more;
+  }
+
+  // dK^T / dV^T accumulators: lane holds d = db*32 + 8*(v/4) + 4*hh + v%4 of key column l32
+  __bf16* __restrict__ dkp = static_cast<__bf16*>(p.dk);
+  __bf16* __restrict__ dvp = static_cast<__bf16*>(p.dv);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int64_t krow = wk0 + kb * 32 + l32;
+    if (krow >= p.Lb) continue;
+    const int64_t off = row_offset(b, static_cast<int64_t>(j) * p.Lb + krow, h, p.Lk, p.H, D);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        bf16x4 k4, v4v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          k4[i] = (__bf16)(dK[db][kb][4 * v4 + i] * p.scale);
+          v4v[i] = (__bf16)(dV[db][kb][4 * v4 + i]);
+        }
+        *reinterpret_cast<bf16x4*>(dkp + off + db * 32 + 8 * v4 + 4 * hh) = k4;
+        *reinterpret_cast<bf16x4*>(dvp + off + db * 32 + 8 * v4 + 4 * hh) = v4v;
+      }
+  }
+}
+
+// ================================================================== launchers
+#define RA_SELECT_FLAGS(CALL)                                                      \
+  do {                                                                             \
+    const bool c_ = p.causal != 0, b_ = p.bias != nullptr, s_ = p.seg != nullptr;  \
+    if (c_) {                                                                      \
+      if (b_) { if (s_) CALL(true, true, true); else CALL(true, true, false); }    \
+      else { if (s_) CALL(true, false, true); else CALL(true, false, false); }     \
+    } else {                                                                       \
+      if (b_) { if (s_) CALL(false, true, true); else CALL(false, true, false); }  \
+      else { if (s_) CALL(false, false, true); else CALL(false, false, false); }   \
+    }                                                                              \
+  } while (0)
+
+template <int D, int NQB>
+hipError_t dq_d(const Params& p, hipStream_t st) {
+  constexpr int BQ = kWaves * 32 * NQB;
+  const int64_t grid = (p.ring_rank < 0 ? p.n_ring : 1) * ((p.Lb + BQ - 1) / BQ) * p.B * p.H;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+#define RA_L(C, B, S) \
+  hipLaunchKernelGGL((dq_mfma_kernel<D, NQB, C, B, S>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
+  RA_SELECT_FLAGS(RA_L);
+#undef RA_L
+  return hipGetLastError();
+}
+
+template <int D, int NKB>
+hipError_t dkdv_d(const Params& p, hipStream_t st) {
+  constexpr int BKW = kWaves * 32 * NKB;
+  const int64_t grid = static_cast<int64_t>(p.n_ring) * ((p.Lb + BKW - 1) / BKW) * p.B * p.H;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+#define RA_L(C, B, S) \
+  hipLaunchKernelGGL((dkdv_mfma_kernel<D, NKB, C, B, S>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
+  RA_SELECT_FLAGS(RA_L);
+#undef RA_L
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t st) {
+  if (p.D == 64) return dq_d<64, 2>(p, st);
+  if (p.D == 128) return dq_d<128, 1>(p, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dkdv_mfma(const Params& p, hipStream_t st) {
+  if (p.D == 64) return dkdv_d<64, 1>(p, st);
+  if (p.D == 128) return dkdv_d<128, 1>(p, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ra

@@ -16,13 +16,11 @@
 // exp2(m_old - m_new).  The rescale is deferred while the new maximum exceeds the
 // stored one by at most kTau (P then stays <= 2^kTau), which is exact because O
 // and l always share the same reference m.
-#include "ra_common.cuh"
+#include "mfma_util.cuh"
 
 namespace ra {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int BK = 64;            // keys per K/V tile
 constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
 
@@ -31,17 +29,6 @@ struct FwdLds {
   static constexpr int SROW = D + 8;          // padded row stride (bf16 elements), 16-byte multiple
   static constexpr int TILE = BK * SROW;
 };
-
-__device__ __forceinline__ bf16x8 lds_read_b128(const __bf16* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
-// Transposed read: within each 16-lane group, lane j receives element (j % 4) of
-// the 4-element chunks addressed by lanes 4e + j/4 for e = 0..3.
-__device__ __forceinline__ i16x4 lds_read_tr(const __bf16* p) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-}
 
 __device__ __forceinline__ float wave_max_pair(float x) {   // max with lane ^ 32
   return fmaxf(x, __shfl_xor(x, 32));

@@ -1,0 +1,69 @@
+// LDS access helpers shared by the MFMA kernels (gfx950, wave64).
+//
+// Operand layouts of v_mfma_f32_32x32x16_bf16 (C = A.B + C, A 32x16, B 16x32):
+//   A: lane l holds A[l % 32][8 * (l / 32) + 0..7]
+//   B: lane l holds B[8 * (l / 32) + 0..7][l % 32]
+//   C: lane l holds C[8 * (v / 4) + 4 * (l / 32) + (v % 4)][l % 32], v = 0..15
+// so a row-major tile read 16 bytes per lane (row = lane % 32) serves as A or
+// as B alike, and a C accumulator feeds the next product as B with its 16
+// values split into two k-steps of 8 (v = 0..7 and 8..15).  The k index of
+// those steps is then the permuted row order {4h + 0..3, 8 + 4h + 0..3} + 16 st
+// (h = l / 32); the matching A operand is read from LDS with the transposing
+// read below, which produces exactly that order.
+#pragma once
+
+#include "ra_common.cuh"
+
+namespace ra {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Transposed read: within each 16-lane group, lane j receives element (j % 4) of
+// the 4-element chunks addressed by lanes 4e + j/4 for e = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr(const __bf16* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// A operand holding the transpose of a row-major LDS tile X (rows = the k index
+// of the product, columns = the A rows): lane l gets
+//   A[l % 32][i] = X[r0 + 16 st + 4 (l / 32) + i][c0 + l % 32]        i = 0..3
+//   A[l % 32][i] = X[r0 + 16 st + 8 + 4 (l / 32) + i - 4][c0 + l % 32] i = 4..7
+// i.e. the k order of a C accumulator's k-step st (see above).  SROW is the
+// tile's row stride in elements.
+template <int SROW>
+__device__ __forceinline__ bf16x8 lds_read_a_transposed(const __bf16* tile, int r0, int st, int c0, int lane) {
+  const int g = lane >> 4, gi = lane & 15, hh = lane >> 5;
+  const int row = r0 + st * 16 + 4 * hh + (gi >> 2);
+  const int col = c0 + 16 * (g & 1) + 4 * (gi & 3);
+  const i16x4 lo = lds_read_tr(tile + row * SROW + col);
+  const i16x4 hi = lds_read_tr(tile + (row + 8) * SROW + col);
+  bf16x8 a;
+  __builtin_memcpy(&a, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
+  return a;
+}
+
+// Pack values v = 8 st .. 8 st + 7 of a C accumulator (already in float) as a
+// bf16 B operand (round to nearest even).
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* e) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = __builtin_convertvector((f32x2){e[2 * i], e[2 * i + 1]}, bf16x2);
+    r[2 * i] = pr[0];
+    r[2 * i + 1] = pr[1];
+  }
+  return r;
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace ra

@@ -136,12 +136,14 @@ size_t workspace_bytes(const Checked& c) {
   return (b + 255) / 256 * 256;
 }
 
+// bfloat16 runs on the MFMA kernels; float32 keeps float32 products throughout (scalar kernels)
 int do_bwd_dkdv(const Checked& c, hipStream_t st) {
-  return hip_status(ra::launch_bwd_dkdv_simt(c.p, st), "dK/dV launch");
+  return hip_status(c.p.bf16 ? ra::launch_bwd_dkdv_mfma(c.p, st) : ra::launch_bwd_dkdv_simt(c.p, st),
+                    "dK/dV launch");
 }
 
 int do_bwd_dq(const Checked& c, hipStream_t st) {
-  return hip_status(ra::launch_bwd_dq_simt(c.p, st), "dQ launch");
+  return hip_status(c.p.bf16 ? ra::launch_bwd_dq_mfma(c.p, st) : ra::launch_bwd_dq_simt(c.p, st), "dQ launch");
 }
 
 }  // namespace
