@@ -24,8 +24,8 @@ namespace {
 // ================================================================== dQ (query tiles stationary)
 constexpr int kBkDq = 64;   // keys per K/V tile
 
-template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
-__global__ __launch_bounds__(kThreads) void dq_mfma_kernel(Params p) {
+template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void dq_mfma_kernel(Params p) {
   constexpr int BK = kBkDq;
   constexpr int QW = 32 * NQB;         // queries per wave
   constexpr int BQ = kWaves * QW;      // queries per workgroup
@@ -277,8 +277,8 @@ __global__ __launch_bounds__(kThreads) void dq_mfma_kernel(Params p) {
 // ================================================================== dK/dV (K/V tiles stationary)
 constexpr int kBqKv = 64;   // queries per LDS tile
 
-template <int D, int NKB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
-__global__ __launch_bounds__(kThreads) void dkdv_mfma_kernel(Params p) {
+template <int D, int NKB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void dkdv_mfma_kernel(Params p) {
   constexpr int BQ = kBqKv;
   constexpr int KW = 32 * NKB;         // keys per wave
   constexpr int BKW = kWaves * KW;     // keys per workgroup
@@ -558,14 +558,16 @@ __global__ __launch_bounds__(kThreads) void dkdv_mfma_kernel(Params p) {
     }                                                                              \
   } while (0)
 
+// head_dim 64 fits two waves per SIMD without spilling; head_dim 128 keeps one
 template <int D, int NQB>
 hipError_t dq_d(const Params& p, hipStream_t st) {
+  constexpr int OCC = D == 64 ? 2 : 1;
   constexpr int BQ = kWaves * 32 * NQB;
   const int64_t grid = (p.ring_rank < 0 ? p.n_ring : 1) * ((p.Lb + BQ - 1) / BQ) * p.B * p.H;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
 #define RA_L(C, B, S) \
-  hipLaunchKernelGGL((dq_mfma_kernel<D, NQB, C, B, S>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
+  hipLaunchKernelGGL((dq_mfma_kernel<D, NQB, C, B, S, OCC>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
   RA_SELECT_FLAGS(RA_L);
 #undef RA_L
   return hipGetLastError();
@@ -573,12 +575,13 @@ hipError_t dq_d(const Params& p, hipStream_t st) {
 
 template <int D, int NKB>
 hipError_t dkdv_d(const Params& p, hipStream_t st) {
+  constexpr int OCC = D == 64 ? 2 : 1;
   constexpr int BKW = kWaves * 32 * NKB;
   const int64_t grid = static_cast<int64_t>(p.n_ring) * ((p.Lb + BKW - 1) / BKW) * p.B * p.H;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
 #define RA_L(C, B, S) \
-  hipLaunchKernelGGL((dkdv_mfma_kernel<D, NKB, C, B, S>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
+  hipLaunchKernelGGL((dkdv_mfma_kernel<D, NKB, C, B, S, OCC>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
   RA_SELECT_FLAGS(RA_L);
 #undef RA_L
   return hipGetLastError();
@@ -587,7 +590,7 @@ hipError_t dkdv_d(const Params& p, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t st) {
-  if (p.D == 64) return dq_d<64, 2>(p, st);
+  if (p.D == 64) return dq_d<64, 1>(p, st);
   if (p.D == 128) return dq_d<128, 1>(p, st);
   return hipErrorInvalidValue;
 }

@@ -30,12 +30,10 @@ struct FwdLds {
   static constexpr int TILE = BK * SROW;
 };
 
-__device__ __forceinline__ float wave_max_pair(float x) {   // max with lane ^ 32
-  return fmaxf(x, __shfl_xor(x, 32));
-}
-
-template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
-__global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(Params p) {
+// OCC: waves per SIMD the register allocation must allow (2 lets one wave's softmax
+// arithmetic run while the other's matrix products do).
+template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_mfma_kernel(Params p) {
   constexpr int QW = 32 * NQB;         // queries per wave
   constexpr int BQ = kWaves * QW;      // queries per workgroup
   constexpr int KK = D / 16;           // k-steps of S^T (head_dim / 16)
@@ -246,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(Params p) {
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[mb][nb][v]);
-        mx = wave_max_pair(mx);
+        mx = pair_max(mx);
         const float mxs = HAS_BIAS ? mx : mx * c;
         // Each row decides for itself whether its maximum grew by more than kTau; the
         // multiply runs only when some row of the wave needs it, with alpha = 1 (exact)
@@ -318,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(Params p) {
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
     const int64_t row = wrow0 + nb * 32 + l32;
-    const float lt = lsum[nb] + __shfl_xor(lsum[nb], 32);
+    const float lt = pair_sum(lsum[nb]);
     if (row >= p.Lb || row < 0) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     __bf16* dst = op + row_offset(b, qrow_base + row, h, p.Lq, p.H, D);
@@ -344,7 +342,9 @@ hipError_t launch_t(const Params& p, hipStream_t st) {
   const int64_t grid = n_qt * p.B * p.H;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, NQB, CAUSAL, HAS_BIAS, HAS_SEG>), dim3(static_cast<unsigned>(grid)),
+  // segment ids cost registers: those variants keep one wave per SIMD rather than spill
+  constexpr int OCC = (HAS_SEG || (HAS_BIAS && D == 64)) ? 1 : 2;
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, NQB, CAUSAL, HAS_BIAS, HAS_SEG, OCC>), dim3(static_cast<unsigned>(grid)),
                      dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }

@@ -62,6 +62,18 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* e) {
   return r;
 }
 
+// Reductions over the lane pair (l, l ^ 32) that shares one column of a C
+// accumulator: v_permlane32_swap exchanges the two halves of the wave, and
+// both results of the swap hold one value of each pair.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
