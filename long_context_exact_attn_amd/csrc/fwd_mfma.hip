@@ -2,8 +2,9 @@
 //
 // One workgroup = 4 wavefronts = one query tile of BQ = 4 * 32 * NQB rows of one
 // (batch, head); the tile stays resident (Q in VGPRs) while the K/V tiles of the
-// ring walk stream through LDS, two buffers deep.  Per K/V tile of BK = 64 keys
-// each wave computes
+// ring walk stream through LDS: direct global -> LDS copies into a ring of stages,
+// issued ahead of use (no staging registers).  Per K/V tile of BK = 64 keys each
+// wave computes
 //   S^T = K . Q^T           v_mfma_f32_32x32x16_bf16, rows = keys, columns = queries
 //   online-softmax update   every lane owns one query column, so row max / row sum are
 //                           in-lane plus one exchange with lane^32
@@ -24,10 +25,13 @@ namespace {
 constexpr int BK = 64;            // keys per K/V tile
 constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
 
+// LDS stages of the K/V ring: three (two tiles in flight) at head_dim 64, two at 128,
+// so that two workgroups fit on a CU either way.
 template <int D>
 struct FwdLds {
-  static constexpr int SROW = D + 8;          // padded row stride (bf16 elements), 16-byte multiple
-  static constexpr int TILE = BK * SROW;
+  static constexpr int NS = D == 64 ? 3 : 2;
+  static constexpr int TILE = BK * D;          // unpadded, swizzled (see swz)
+  static constexpr int NSEG = TILE * 2 / 1024 / kWaves;   // 1 KiB direct-load segments per wave per tile
 };
 
 // OCC: waves per SIMD the register allocation must allow (2 lets one wave's softmax
@@ -38,19 +42,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   constexpr int BQ = kWaves * QW;      // queries per workgroup
   constexpr int KK = D / 16;           // k-steps of S^T (head_dim / 16)
   constexpr int DB = D / 32;           // 32-row blocks of O^T
-  constexpr int SROW = FwdLds<D>::SROW;
+  constexpr int NS = FwdLds<D>::NS;
   constexpr int TILE = FwdLds<D>::TILE;
-  constexpr int CPR = D / 8;           // 16-byte chunks per row
-  constexpr int CPT = BK * CPR / kThreads;   // chunks per thread per tile
-  static_assert(CPT * kThreads == BK * CPR, "tile load must divide evenly");
+  constexpr int NSEG = FwdLds<D>::NSEG;
+  static_assert(NSEG * 1024 * kWaves == TILE * 2, "tile must split into 1 KiB segments");
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][TILE];
-  __shared__ float sBias[2][BK];
-  __shared__ __attribute__((aligned(16))) int sSeg[2][BK];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[NS][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[NS][TILE];
+  __shared__ float sBias[NS][BK];
+  __shared__ __attribute__((aligned(16))) int sSeg[NS][BK];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-derived values stay scalar
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -112,26 +115,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     for (int db = 0; db < DB; ++db) O[db][nb] = f32x16{};
   }
 
-  // ---- K/V tile staging: global -> registers -> LDS (two buffers)
-  uint4 kreg[CPT], vreg[CPT];
+  // ---- K/V tile staging: direct global -> LDS copies into a ring of NS stages, issued
+  // NS - 1 tiles ahead.  Each wave copies NSEG 1 KiB segments of K and of V per tile; the
+  // lane that lands at segment byte 16 l fetches the chunk the swizzle puts there.  The
+  // tile's base address is wave-uniform; rows past the end of a ragged tile fetch row 0
+  // instead (finite values that the masks give zero weight).
+  const int64_t kv_bh = (static_cast<int64_t>(b) * p.Lk * p.H + h) * D;   // (b, key 0, h)
+  const int64_t kstride = static_cast<int64_t>(p.H) * D;                 // elements per key
+  int grow_[NSEG], goff[NSEG], goff0[NSEG];
+#pragma unroll
+  for (int j = 0; j < NSEG; ++j) {
+    const int byte = (wave * NSEG + j) * 1024 + lane * 16;
+    const int row = byte / (2 * D);
+    const int chunk = ((byte % (2 * D)) >> 4) ^ (row & 7);
+    grow_[j] = row;
+    goff[j] = row * static_cast<int>(kstride) + chunk * 8;   // < 64 * H * D, checked on the host
+    goff0[j] = chunk * 8;
+  }
   float breg = 0.f;
   int sreg = 0;
-  auto load_tile = [&](int64_t key0, int64_t kend) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx / CPR;
-      const int col = (cidx % CPR) * 8;
-      const int64_t key = key0 + row;
-      if (key < kend) {
-        const int64_t off = row_offset(b, key, h, p.Lk, p.H, D) + col;
-        kreg[i] = *reinterpret_cast<const uint4*>(kp + off);
-        vreg[i] = *reinterpret_cast<const uint4*>(vp + off);
-      } else {
-        kreg[i] = uint4{0, 0, 0, 0};
-        vreg[i] = uint4{0, 0, 0, 0};
-      }
-    }
+  // bias / segment ids of the tile (plain loads, stored by store_small before the barrier)
+  auto load_small = [&](int64_t key0, int64_t kend) {
     if (tid < BK) {
       const int64_t key = key0 + tid;
       if constexpr (HAS_BIAS)
@@ -139,39 +143,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       if constexpr (HAS_SEG) sreg = key < kend ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx / CPR;
-      const int col = (cidx % CPR) * 8;
-      *reinterpret_cast<uint4*>(&sK[buf][row * SROW + col]) = kreg[i];
-      *reinterpret_cast<uint4*>(&sV[buf][row * SROW + col]) = vreg[i];
-    }
+  auto store_small = [&](int slot) {
     if (tid < BK) {
-      if constexpr (HAS_BIAS) sBias[buf][tid] = breg;
-      if constexpr (HAS_SEG) sSeg[buf][tid] = sreg;
+      if constexpr (HAS_BIAS) sBias[slot][tid] = breg;
+      if constexpr (HAS_SEG) sSeg[slot][tid] = sreg;
+    }
+  };
+  auto issue_kv = [&](int64_t key0, int64_t kend, int slot) {
+    const __bf16* kb = kp + kv_bh + key0 * kstride;
+    const __bf16* vb = vp + kv_bh + key0 * kstride;
+    const bool full = key0 + BK <= kend;
+    const int nvalid = static_cast<int>(kend - key0);
+#pragma unroll
+    for (int j = 0; j < NSEG; ++j) {
+      const int off = (full || grow_[j] < nvalid) ? goff[j] : goff0[j];
+      dma16(kb + off, &sK[slot][(wave * NSEG + j) * 512]);
+      dma16(vb + off, &sV[slot][(wave * NSEG + j) * 512]);
     }
   };
 
+  // ring walk with NS - 1 tiles of lookahead: T[0] is being computed, T[NS-1] is issued
   RingWalk walk;
   walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
-  bool have = nrows > 0 && walk.next<BK>();
-  int buf = 0;
-  int64_t key0 = 0, kend = 0;
-  if (have) {
-    key0 = walk.key0;
-    kend = walk.kend;
-    load_tile(key0, kend);
-    store_tile(0);
+  int64_t tk0[NS], tke[NS];
+  bool tok[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    tok[i] = nrows > 0 && walk.next<BK>();
+    tk0[i] = walk.key0;
+    tke[i] = walk.kend;
   }
+  // prologue: the first NS - 1 tiles
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (tok[i]) {
+      load_small(tk0[i], tke[i]);
+      issue_kv(tk0[i], tke[i], i);
+      store_small(i);
+    }
+  RA_WAIT_VMCNT(0);
   __syncthreads();
 
-  while (have) {
-    const bool more = walk.next<BK>();
-    const int64_t nkey0 = walk.key0, nkend = walk.kend;
-    if (more) load_tile(nkey0, nkend);   // in flight while this tile is computed
-
+  int slot = 0;
+  while (tok[0]) {
+    const int64_t key0 = tk0[0], kend = tke[0];
+    const int ahead = slot + NS - 1 >= NS ? slot - 1 : slot + NS - 1;   // (slot + NS - 1) % NS
+    const bool issue = tok[NS - 1];
+    if (issue) {
+      load_small(tk0[NS - 1], tke[NS - 1]);   // before the copies: its wait then spares them
+      issue_kv(tk0[NS - 1], tke[NS - 1], ahead);
+    }
+    const int buf = slot;
     const __bf16* Kt = sK[buf];
     const __bf16* Vt = sV[buf];
     const bool wave_active = wvalid > 0 && !(CAUSAL && key0 > wpos0 + (wvalid < QW ? wvalid : QW) - 1);
@@ -186,7 +208,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 a = lds_read_b128(Kt + (mb * 32 + l32) * SROW + 16 * kk + 8 * hh);
+          const bf16x8 a = lds_read_swz<D>(Kt, mb * 32 + l32, 2 * kk + hh);
 #pragma unroll
           for (int nb = 0; nb < NQB; ++nb)
             S[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Qf[nb][kk], S[mb][nb], 0, 0, 0);
@@ -259,7 +281,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
           m[nb] = mnew;
         }
         const float msub = (m[nb] == -INFINITY) ? 0.f : m[nb];
-        float rs = 0.f;
+        float acc[2][2];   // row sum in independent partial sums (no serial dependency chain)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -269,46 +291,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
             for (int i = 0; i < 8; ++i) {
               const float x = S[mb][nb][8 * st + i];
               e[i] = HAS_BIAS ? __builtin_amdgcn_exp2f(x - msub) : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -msub));
-              rs += e[i];
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const bf16x2 pr = __builtin_convertvector((f32x2){e[2 * i], e[2 * i + 1]}, bf16x2);
-              P[nb][mb][st][2 * i] = pr[0];
-              P[nb][mb][st][2 * i + 1] = pr[1];
-            }
+            P[nb][mb][st] = pack_bf16x8(e);
+            acc[mb][st] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
           }
-        lsum[nb] += rs;
+        lsum[nb] += (acc[0][0] + acc[0][1]) + (acc[1][0] + acc[1][1]);
       }
 
       // ---- O^T += V^T . P^T ; V^T operand through transposed LDS reads
-      const int g = lane >> 4, gi = lane & 15;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int rbase = mb * 32 + st * 16 + 4 * hh + (gi >> 2);
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const int col = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
-            const i16x4 lo = lds_read_tr(Vt + rbase * SROW + col);
-            const i16x4 hi = lds_read_tr(Vt + (rbase + 8) * SROW + col);
-            bf16x8 a;
-            __builtin_memcpy(&a, &lo, 8);
-            __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
+            const bf16x8 a = lds_read_a_transposed_swz<D>(Vt, mb * 32, st, db * 32, lane);
 #pragma unroll
-            for (int nb = 0; nb < NQB; ++nb)
-              O[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[nb][mb][st], O[db][nb], 0, 0, 0);
+            for (int nb = 0; nb < NQB; ++nb) O[db][nb] = mfma32(a, P[nb][mb][st], O[db][nb]);
           }
-        }
     }
 
-    if (more) store_tile(buf ^ 1);
+    // the next tile's copies (issued NS - 2 iterations ago) must have landed; the ones
+    // issued this iteration may stay in flight
+    if (issue) {
+      store_small(ahead);
+      if constexpr (NS == 3) {
+        RA_WAIT_VMCNT(2 * NSEG);
+      } else {
+        RA_WAIT_VMCNT(0);
+      }
+    } else {
+      RA_WAIT_VMCNT(0);
+    }
     __syncthreads();
-    buf ^= 1;
-    key0 = nkey0;
-    kend = nkend;
-    have = more;
+    slot = slot + 1 == NS ? 0 : slot + 1;
+#pragma unroll
+    for (int i = 0; i + 1 < NS; ++i) {
+      tok[i] = tok[i + 1];
+      tk0[i] = tk0[i + 1];
+      tke[i] = tke[i + 1];
+    }
+    tok[NS - 1] = walk.next<BK>();
+    tk0[NS - 1] = walk.key0;
+    tke[NS - 1] = walk.kend;
   }
 
   // ---- epilogue: out = O / l, lse = m + log l (natural log)

@@ -49,6 +49,52 @@ __device__ __forceinline__ bf16x8 lds_read_a_transposed(const __bf16* tile, int 
   return a;
 }
 
+// ---- swizzled unpadded tiles: a row of D bf16 holds D / 8 chunks of 16 bytes, and
+// chunk c of row r is stored at chunk position c ^ (r & 7).  Eight consecutive rows
+// then spread any one chunk over eight distinct positions, so the 16-byte operand
+// reads of 8 lanes (rows r..r+7) and the transposing reads below touch distinct banks,
+// without padding (which direct global -> LDS loads cannot produce).
+template <int D>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * D + ((chunk ^ (row & 7)) << 3);
+}
+
+// 16-byte operand read of row `row`, chunk `chunk` of a swizzled tile.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_read_swz(const __bf16* tile, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(tile + swz<D>(row, chunk));
+}
+
+// lds_read_a_transposed for a swizzled tile (same result layout).
+template <int D>
+__device__ __forceinline__ bf16x8 lds_read_a_transposed_swz(const __bf16* tile, int r0, int st, int c0, int lane) {
+  const int g = lane >> 4, gi = lane & 15, hh = lane >> 5;
+  const int row = r0 + st * 16 + 4 * hh + (gi >> 2);
+  const int col = c0 + 16 * (g & 1) + 4 * (gi & 3);      // element column; 4 elements = 8 bytes
+  const int within = col & 7;                             // 0 or 4
+  const i16x4 lo = lds_read_tr(tile + swz<D>(row, col >> 3) + within);
+  const i16x4 hi = lds_read_tr(tile + swz<D>(row + 8, col >> 3) + within);
+  bf16x8 a;
+  __builtin_memcpy(&a, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
+  return a;
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16 l
+// (lds must be wave-uniform).  Completion is counted by vmcnt only, and the copy is
+// issued through inline assembly so that the compiler does not treat it as an LDS
+// store: it would otherwise wait for every copy in flight before any LDS read and at
+// every barrier.  Callers wait with RA_WAIT_VMCNT and a barrier before the data is read.
+__device__ __forceinline__ void dma16(const void* g, __bf16* lds) {
+  const unsigned dst = static_cast<unsigned>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) void*)lds));
+  // (one wait state between the M0 write and the copy that reads it)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(dst), "v"(g) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding).
+#define RA_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
+
 // Pack values v = 8 st .. 8 st + 7 of a C accumulator (already in float) as a
 // bf16 B operand (round to nearest even).
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float* e) {

@@ -71,6 +71,9 @@ int check_shape(const ra_shape* s, int32_t n_ring, Checked* c) {
   if (std::isnan(s->scale)) return fail(RA_ERR_ARG, "scale is NaN");
   const int64_t HB = static_cast<int64_t>(s->batch) * s->heads;
   if (HB > (int64_t(1) << 30)) return fail(RA_ERR_SHAPE, "batch*heads too large");
+  // the kernels address the rows of one 64-key tile with 32-bit offsets
+  if (static_cast<int64_t>(s->heads) * s->head_dim * 64 >= (int64_t(1) << 31))
+    return fail(RA_ERR_SHAPE, "heads*head_dim too large (%lld)", (long long)s->heads * s->head_dim);
   ra::Params& p = c->p;
   p = ra::Params{};
   p.Lq = s->q_len;
