@@ -31,19 +31,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   constexpr int BQ = kWaves * QW;      // queries per workgroup
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
-  constexpr int SROW = D + 8;
-  constexpr int TILE = BK * SROW;
-  constexpr int CPR = D / 8;
-  constexpr int CPT = BK * CPR / kThreads;
-  static_assert(CPT * kThreads == BK * CPR, "tile load must divide evenly");
+#ifndef RA_DQ_NS
+#define RA_DQ_NS 2
+#endif
+  constexpr int NS = D == 64 ? RA_DQ_NS : 2;  // LDS stages of the K/V ring
+  constexpr int TILE = BK * D;         // unpadded, swizzled
+  constexpr int NSEG = TILE * 2 / 1024 / kWaves;   // 1 KiB direct-copy segments per wave per tile
+  static_assert(NSEG * 1024 * kWaves == TILE * 2, "tile must split into 1 KiB segments");
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][TILE];
-  __shared__ float sBias[2][BK];
-  __shared__ __attribute__((aligned(16))) int sSeg[2][BK];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[NS][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[NS][TILE];
+  __shared__ float sBias[NS][BK];
+  __shared__ __attribute__((aligned(16))) int sSeg[NS][BK];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -101,25 +103,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) dQ[db][nb] = f32x16{};
 
-  uint4 kreg[CPT], vreg[CPT];
+  // K/V tiles: direct global -> LDS copies into a ring of NS stages, as in the forward
+  const int64_t kv_bh = (static_cast<int64_t>(b) * p.Lk * p.H + h) * D;
+  const int64_t kstride = static_cast<int64_t>(p.H) * D;
+  int grow_[NSEG], goff[NSEG], goff0[NSEG];
+#pragma unroll
+  for (int jj = 0; jj < NSEG; ++jj) {
+    const int byte = (wave * NSEG + jj) * 1024 + lane * 16;
+    const int row = byte / (2 * D);
+    const int chunk = ((byte % (2 * D)) >> 4) ^ (row & 7);
+    grow_[jj] = row;
+    goff[jj] = row * static_cast<int>(kstride) + chunk * 8;   // < 64 * H * D, checked on the host
+    goff0[jj] = chunk * 8;
+  }
   float breg = 0.f;
   int sreg = 0;
-  auto load_tile = [&](int64_t key0, int64_t kend) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx / CPR;
-      const int col = (cidx % CPR) * 8;
-      const int64_t key = key0 + row;
-      if (key < kend) {
-        const int64_t off = row_offset(b, key, h, p.Lk, p.H, D) + col;
-        kreg[i] = *reinterpret_cast<const uint4*>(kp + off);
-        vreg[i] = *reinterpret_cast<const uint4*>(vp + off);
-      } else {
-        kreg[i] = uint4{0, 0, 0, 0};
-        vreg[i] = uint4{0, 0, 0, 0};
-      }
-    }
+  auto load_small = [&](int64_t key0, int64_t kend) {
     if (tid < BK) {
       const int64_t key = key0 + tid;
       if constexpr (HAS_BIAS)
@@ -127,38 +126,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       if constexpr (HAS_SEG) sreg = key < kend ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx / CPR;
-      const int col = (cidx % CPR) * 8;
-      *reinterpret_cast<uint4*>(&sK[buf][row * SROW + col]) = kreg[i];
-      *reinterpret_cast<uint4*>(&sV[buf][row * SROW + col]) = vreg[i];
-    }
+  auto store_small = [&](int slot) {
     if (tid < BK) {
-      if constexpr (HAS_BIAS) sBias[buf][tid] = breg;
-      if constexpr (HAS_SEG) sSeg[buf][tid] = sreg;
+      if constexpr (HAS_BIAS) sBias[slot][tid] = breg;
+      if constexpr (HAS_SEG) sSeg[slot][tid] = sreg;
+    }
+  };
+  auto issue_kv = [&](int64_t key0, int64_t kend, int slot) {
+    const __bf16* kb = kp + kv_bh + key0 * kstride;
+    const __bf16* vb = vp + kv_bh + key0 * kstride;
+    const bool full = key0 + BK <= kend;
+    const int nvalid = static_cast<int>(kend - key0);
+#pragma unroll
+    for (int jj = 0; jj < NSEG; ++jj) {
+      const int off = (full || grow_[jj] < nvalid) ? goff[jj] : goff0[jj];
+      dma16(kb + off, &sK[slot][(wave * NSEG + jj) * 512]);
+      dma16(vb + off, &sV[slot][(wave * NSEG + jj) * 512]);
     }
   };
 
   RingWalk walk;
   walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
-  bool have = nrows > 0 && walk.next<BK>();
-  int buf = 0;
-  int64_t key0 = 0, kend = 0;
-  if (have) {
-    key0 = walk.key0;
-    kend = walk.kend;
-    load_tile(key0, kend);
-    store_tile(0);
+  int64_t tk0[NS], tke[NS];
+  bool tok[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    tok[i] = nrows > 0 && walk.next<BK>();
+    tk0[i] = walk.key0;
+    tke[i] = walk.kend;
   }
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (tok[i]) {
+      load_small(tk0[i], tke[i]);
+      issue_kv(tk0[i], tke[i], i);
+      store_small(i);
+    }
+  RA_WAIT_VMCNT(0);
   __syncthreads();
 
-  while (have) {
-    const bool more = walk.next<BK>();
-    const int64_t nkey0 = walk.key0, nkend = walk.kend;
-    if (more) load_tile(nkey0, nkend);
+  int slot = 0;
+  while (tok[0]) {
+    const int64_t key0 = tk0[0], kend = tke[0];
+    const int ahead = slot + NS - 1 >= NS ? slot - 1 : slot + NS - 1;   // (slot + NS - 1) % NS
+    const bool issue = tok[NS - 1];
+    if (issue) {
+      load_small(tk0[NS - 1], tke[NS - 1]);
+      issue_kv(tk0[NS - 1], tke[NS - 1], ahead);
+    }
+    const int buf = slot;
 
     const __bf16* Kt = sK[buf];
     const __bf16* Vt = sV[buf];
@@ -176,8 +192,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 ak = lds_read_b128(Kt + (mb * 32 + l32) * SROW + 16 * kk + 8 * hh);
-          const bf16x8 av = lds_read_b128(Vt + (mb * 32 + l32) * SROW + 16 * kk + 8 * hh);
+          const bf16x8 ak = lds_read_swz<D>(Kt, mb * 32 + l32, 2 * kk + hh);
+          const bf16x8 av = lds_read_swz<D>(Vt, mb * 32 + l32, 2 * kk + hh);
 #pragma unroll
           for (int nb = 0; nb < NQB; ++nb) {
             S[mb][nb] = mfma32(ak, Qf[nb][kk], S[mb][nb]);
@@ -242,18 +258,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const bf16x8 a = lds_read_a_transposed<SROW>(Kt, mb * 32, st, db * 32, lane);
+            const bf16x8 a = lds_read_a_transposed_swz<D>(Kt, mb * 32, st, db * 32, lane);
 #pragma unroll
             for (int nb = 0; nb < NQB; ++nb) dQ[db][nb] = mfma32(a, dS[nb][mb][st], dQ[db][nb]);
           }
     }
 
-    if (more) store_tile(buf ^ 1);
+    if (issue) {
+      store_small(ahead);
+      if constexpr (NS == 3) {
+        RA_WAIT_VMCNT(2 * NSEG);
+      } else {
+        RA_WAIT_VMCNT(0);
+      }
+    } else {
+      RA_WAIT_VMCNT(0);
+    }
     __syncthreads();
-    buf ^= 1;
-    key0 = nkey0;
-    kend = nkend;
-    have = more;
+    slot = slot + 1 == NS ? 0 : slot + 1;
+#pragma unroll
+    for (int i = 0; i + 1 < NS; ++i) {
+      tok[i] = tok[i + 1];
+      tk0[i] = tk0[i + 1];
+      tke[i] = tke[i + 1];
+    }
+    tok[NS - 1] = walk.next<BK>();
+    tk0[NS - 1] = walk.key0;
+    tke[NS - 1] = walk.kend;
   }
 
   __bf16* __restrict__ dqp = static_cast<__bf16*>(p.dq);
@@ -284,21 +315,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   constexpr int BKW = kWaves * KW;     // keys per workgroup
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
-  constexpr int SROW = D + 8;
-  constexpr int TILE = BQ * SROW;
-  constexpr int CPR = D / 8;
-  constexpr int CPT = BQ * CPR / kThreads;
-  static_assert(CPT * kThreads == BQ * CPR, "tile load must divide evenly");
+#ifndef RA_KV_NS
+#define RA_KV_NS 2
+#endif
+  constexpr int NS = D == 64 ? RA_KV_NS : 2;  // LDS stages of the query-tile ring
+  constexpr int TILE = BQ * D;         // unpadded, swizzled
+  constexpr int NSEG = TILE * 2 / 1024 / kWaves;   // 1 KiB direct-copy segments per wave per tile
+  static_assert(NSEG * 1024 * kWaves == TILE * 2, "tile must split into 1 KiB segments");
   static_assert(BQ == 64, "two 32-query blocks per tile");
 
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sG[2][TILE];
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];    // -lse * log2e (-inf: row contributes nothing)
-  __shared__ __attribute__((aligned(16))) float sDl[2][BQ];   // Delta
-  __shared__ __attribute__((aligned(16))) int sSg[2][BQ];     // segment id of the query
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[NS][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sG[NS][TILE];
+  __shared__ __attribute__((aligned(16))) float sL[NS][BQ];    // -lse * log2e (-inf: row contributes nothing)
+  __shared__ __attribute__((aligned(16))) float sDl[NS][BQ];   // Delta
+  __shared__ __attribute__((aligned(16))) int sSg[NS][BQ];     // segment id of the query
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -353,26 +386,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       dV[db][kb] = f32x16{};
     }
 
-  // ---- query tile staging: global -> registers -> LDS (two buffers)
-  uint4 qreg[CPT], greg[CPT];
+  // ---- query tile staging: direct global -> LDS copies of Q and dO into a ring of NS
+  // stages, issued NS - 1 tiles ahead (rows past the rank's end fetch the tile's row 0:
+  // finite values whose -inf lse gives them zero weight); lse, Delta and segment ids of
+  // the tile go through registers.
+  const int64_t qstride = static_cast<int64_t>(p.H) * D;
+  const int64_t q_bh = (static_cast<int64_t>(b) * p.Lq * p.H + h) * D;   // (b, row 0, h)
+  int grow_[NSEG], goff[NSEG], goff0[NSEG];
+#pragma unroll
+  for (int jj = 0; jj < NSEG; ++jj) {
+    const int byte = (wave * NSEG + jj) * 1024 + lane * 16;
+    const int row = byte / (2 * D);
+    const int chunk = ((byte % (2 * D)) >> 4) ^ (row & 7);
+    grow_[jj] = row;
+    goff[jj] = row * static_cast<int>(qstride) + chunk * 8;   // < 64 * H * D, checked on the host
+    goff0[jj] = chunk * 8;
+  }
   float lreg = 0.f, dreg = 0.f;
   int sreg = 0;
-  auto load_tile = [&](int64_t row0, int64_t rend, int64_t pbase) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx / CPR;
-      const int col = (cidx % CPR) * 8;
-      const int64_t r = row0 + row;
-      if (r < rend) {
-        const int64_t off = row_offset(b, r, h, p.Lq, p.H, D) + col;
-        qreg[i] = *reinterpret_cast<const uint4*>(qp + off);
-        greg[i] = *reinterpret_cast<const uint4*>(gp + off);
-      } else {
-        qreg[i] = uint4{0, 0, 0, 0};
-        greg[i] = uint4{0, 0, 0, 0};
-      }
-    }
+  auto load_small = [&](int64_t row0, int64_t rend, int64_t pbase) {
     if (tid < BQ) {
       const int64_t r = row0 + tid;
       const bool ok = r < rend;
@@ -383,41 +415,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       if constexpr (HAS_SEG) sreg = ok ? p.seg[static_cast<int64_t>(b) * p.Lk + pbase + r] : 0;
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx / CPR;
-      const int col = (cidx % CPR) * 8;
-      *reinterpret_cast<uint4*>(&sQ[buf][row * SROW + col]) = qreg[i];
-      *reinterpret_cast<uint4*>(&sG[buf][row * SROW + col]) = greg[i];
-    }
+  auto store_small = [&](int slot) {
     if (tid < BQ) {
-      sL[buf][tid] = lreg;
-      sDl[buf][tid] = dreg;
-      if constexpr (HAS_SEG) sSg[buf][tid] = sreg;
+      sL[slot][tid] = lreg;
+      sDl[slot][tid] = dreg;
+      if constexpr (HAS_SEG) sSg[slot][tid] = sreg;
+    }
+  };
+  auto issue_qg = [&](int64_t row0, int64_t rend, int slot) {
+    const __bf16* qb_ = qp + q_bh + row0 * qstride;
+    const __bf16* gb_ = gp + q_bh + row0 * qstride;
+    const bool full = row0 + BQ <= rend;
+    const int nvalid = static_cast<int>(rend - row0);
+#pragma unroll
+    for (int jj = 0; jj < NSEG; ++jj) {
+      const int off = (full || grow_[jj] < nvalid) ? goff[jj] : goff0[jj];
+      dma16(qb_ + off, &sQ[slot][(wave * NSEG + jj) * 512]);
+      dma16(gb_ + off, &sG[slot][(wave * NSEG + jj) * 512]);
     }
   };
 
+  // query walk with NS - 1 tiles of lookahead: entry 0 is computed, entry NS - 1 is issued
   QueryWalk walk;
   walk.begin(p.n_ring, j, p.Lb, CAUSAL, kfirst, p.ring_rank);
-  bool have = walk.next<BQ>();
-  int buf = 0;
-  int64_t row0 = 0, rend = 0, pbase = 0;
-  if (have) {
-    row0 = walk.row0;
-    rend = walk.rend;
-    pbase = walk.pos_base;
-    load_tile(row0, rend, pbase);
-    store_tile(0);
+  int64_t tr0[NS], tre[NS], tpb[NS];
+  bool tok[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    tok[i] = walk.next<BQ>();
+    tr0[i] = walk.row0;
+    tre[i] = walk.rend;
+    tpb[i] = walk.pos_base;
   }
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (tok[i]) {
+      load_small(tr0[i], tre[i], tpb[i]);
+      issue_qg(tr0[i], tre[i], i);
+      store_small(i);
+    }
+  RA_WAIT_VMCNT(0);
   __syncthreads();
 
-  while (have) {
-    const bool more = walk.next<BQ>();
-    const int64_t nrow0 = walk.row0, nrend = walk.rend, npbase = walk.pos_base;
-    if (more) load_tile(nrow0, nrend, npbase);
-
+  int slot = 0;
+  while (tok[0]) {
+    const int64_t row0 = tr0[0], rend = tre[0], pbase = tpb[0];
+    const int ahead = slot + NS - 1 >= NS ? slot - 1 : slot + NS - 1;   // (slot + NS - 1) % NS
+    const bool issue = tok[NS - 1];
+    if (issue) {
+      load_small(tr0[NS - 1], tre[NS - 1], tpb[NS - 1]);   // before the copies: its wait spares them
+      issue_qg(tr0[NS - 1], tre[NS - 1], ahead);
+    }
+    const int buf = slot;
     const __bf16* Qt = sQ[buf];
     const __bf16* Gt = sG[buf];
     const int64_t qpos0 = row0 + pbase;                      // global position of the tile's row 0
@@ -443,8 +492,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 aq = lds_read_b128(Qt + (qb * 32 + l32) * SROW + 16 * kk + 8 * hh);
-          const bf16x8 ag = lds_read_b128(Gt + (qb * 32 + l32) * SROW + 16 * kk + 8 * hh);
+          const bf16x8 aq = lds_read_swz<D>(Qt, qb * 32 + l32, 2 * kk + hh);
+          const bf16x8 ag = lds_read_swz<D>(Gt, qb * 32 + l32, 2 * kk + hh);
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
             S[kb] = mfma32(aq, Kf[kb][kk], S[kb]);
@@ -501,8 +550,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const bf16x8 ag = lds_read_a_transposed<SROW>(Gt, qb * 32, st, db * 32, lane);
-            const bf16x8 aq = lds_read_a_transposed<SROW>(Qt, qb * 32, st, db * 32, lane);
+            const bf16x8 ag = lds_read_a_transposed_swz<D>(Gt, qb * 32, st, db * 32, lane);
+            const bf16x8 aq = lds_read_a_transposed_swz<D>(Qt, qb * 32, st, db * 32, lane);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
               dV[db][kb] = mfma32(ag, Pb[kb][st], dV[db][kb]);
@@ -512,13 +561,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       }
     }
 
-    if (more) store_tile(buf ^ 1);
+    // the next tile's copies must have landed; this iteration's may stay in flight
+    if (issue) {
+      store_small(ahead);
+      if constexpr (NS == 3) {
+        RA_WAIT_VMCNT(2 * NSEG);
+      } else {
+        RA_WAIT_VMCNT(0);
+      }
+    } else {
+      RA_WAIT_VMCNT(0);
+    }
     __syncthreads();
-    buf ^= 1;
-    row0 = nrow0;
-    rend = nrend;
-    pbase = npbase;
-    have = more;
+    slot = slot + 1 == NS ? 0 : slot + 1;
+#pragma unroll
+    for (int i = 0; i + 1 < NS; ++i) {
+      tok[i] = tok[i + 1];
+      tr0[i] = tr0[i + 1];
+      tre[i] = tre[i + 1];
+      tpb[i] = tpb[i + 1];
+    }
+    tok[NS - 1] = walk.next<BQ>();
+    tr0[NS - 1] = walk.row0;
+    tre[NS - 1] = walk.rend;
+    tpb[NS - 1] = walk.pos_base;
   }
 
   // dK^T / dV^T accumulators: lane holds d = db*32 + 8*(v/4) + 4*hh + v%4 of key column l32

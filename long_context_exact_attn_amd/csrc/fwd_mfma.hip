@@ -25,11 +25,14 @@ namespace {
 constexpr int BK = 64;            // keys per K/V tile
 constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
 
-// LDS stages of the K/V ring: three (two tiles in flight) at head_dim 64, two at 128,
-// so that two workgroups fit on a CU either way.
+// LDS stages of the K/V ring (two: one tile in flight while one is computed; a third
+// stage measured slower at head_dim 64).
 template <int D>
 struct FwdLds {
-  static constexpr int NS = D == 64 ? 3 : 2;
+#ifndef RA_FWD_NS
+#define RA_FWD_NS 2
+#endif
+  static constexpr int NS = D == 64 ? RA_FWD_NS : 2;
   static constexpr int TILE = BK * D;          // unpadded, swizzled (see swz)
   static constexpr int NSEG = TILE * 2 / 1024 / kWaves;   // 1 KiB direct-load segments per wave per tile
 };
