@@ -23,6 +23,41 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s (fwd, fwd+bwd) at 1 MI355X and % of bf16 MFMA peak"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    """Hash of every kernel source file: HBM counter figures are valid only for this exact code."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_exact_attn_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.cuh"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` (calibrated FETCH_SIZE + WRITE_SIZE) recorded in
+    profiles/traffic_<workload>.txt, or None when absent or taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec, cur = {}, None
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("source:"):
+                rec["source"] = line.split(":", 1)[1].strip()
+            elif line.startswith("kernel:"):
+                cur = line.split(":", 1)[1].strip()
+            elif line.startswith("hbm_bytes:") and cur:
+                rec[cur] = int(float(line.split(":", 1)[1]))
+    if rec.get("source") != kernel_source_hash():
+        return None
+    return rec.get(kernel)
 
 
 def parse():
@@ -34,6 +69,7 @@ def parse():
     ap.add_argument("--fwd-only", action="store_true", help="time the forward alone (not the bench line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, run one plain device copy of this many MiB (a known-size kernel "
                          "that calibrates the profiler's HBM byte counters)")
@@ -79,6 +115,9 @@ def cpu_baseline(w, t, target_s):
 
 def main():
     args = parse()
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(the ring's K/V exchange across devices is not built); run with --gpus 1", file=sys.stderr)
@@ -190,7 +229,8 @@ def main():
         "visible_pairs": pairs * w.heads,
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": M.PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ach / M.PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(ach / M.PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name, dom)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)

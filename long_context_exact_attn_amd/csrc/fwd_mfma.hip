@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   __shared__ __attribute__((aligned(16))) __bf16 sV[NS][TILE];
   __shared__ float sBias[NS][BK];
   __shared__ __attribute__((aligned(16))) int sSeg[NS][BK];
+  __shared__ int sSegRange[NS][2];   // smallest and largest segment id among the tile's keys
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-derived values stay scalar
@@ -99,12 +100,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     }
   }
   int qseg[NQB];
+  int qseg_lo = 0, qseg_hi = 0;   // range of the wave's query segment ids
   if constexpr (HAS_SEG) {
+    int lo = INT32_MAX, hi = INT32_MIN;
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) {
       int64_t pos = wpos0 + nb * 32 + l32;
-      qseg[nb] = (wrow0 + nb * 32 + l32 < p.Lb) ? p.seg[static_cast<int64_t>(b) * p.Lk + pos] : 0;
+      const bool ok = wrow0 + nb * 32 + l32 < p.Lb;
+      qseg[nb] = ok ? p.seg[static_cast<int64_t>(b) * p.Lk + pos] : 0;
+      lo = ok ? min(lo, qseg[nb]) : lo;
+      hi = ok ? max(hi, qseg[nb]) : hi;
     }
+    qseg_lo = __builtin_amdgcn_readfirstlane(wave_min_i32(lo));
+    qseg_hi = __builtin_amdgcn_readfirstlane(wave_max_i32(hi));
   }
 
   const float c = p.scale * kLog2e;   // raw score -> log2 units
@@ -146,10 +154,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       if constexpr (HAS_SEG) sreg = key < kend ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
     }
   };
-  auto store_small = [&](int slot) {
+  auto store_small = [&](int slot, int64_t key0, int64_t kend) {
     if (tid < BK) {
       if constexpr (HAS_BIAS) sBias[slot][tid] = breg;
-      if constexpr (HAS_SEG) sSeg[slot][tid] = sreg;
+      if constexpr (HAS_SEG) {
+        sSeg[slot][tid] = sreg;
+        // the tile's id range lets a wave skip a tile that shares no segment with its queries
+        const bool ok = key0 + tid < kend;
+        const int lo = wave_min_i32(ok ? sreg : INT32_MAX);
+        const int hi = wave_max_i32(ok ? sreg : INT32_MIN);
+        if (tid == 0) {
+          sSegRange[slot][0] = lo;
+          sSegRange[slot][1] = hi;
+        }
+      }
     }
   };
   auto issue_kv = [&](int64_t key0, int64_t kend, int slot) {
@@ -182,7 +200,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     if (tok[i]) {
       load_small(tk0[i], tke[i]);
       issue_kv(tk0[i], tke[i], i);
-      store_small(i);
+      store_small(i, tk0[i], tke[i]);
     }
   RA_WAIT_VMCNT(0);
   __syncthreads();
@@ -199,7 +217,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     const int buf = slot;
     const __bf16* Kt = sK[buf];
     const __bf16* Vt = sV[buf];
-    const bool wave_active = wvalid > 0 && !(CAUSAL && key0 > wpos0 + (wvalid < QW ? wvalid : QW) - 1);
+    bool wave_active = wvalid > 0 && !(CAUSAL && key0 > wpos0 + (wvalid < QW ? wvalid : QW) - 1);
+    if constexpr (HAS_SEG) {
+      // no key of the tile shares a segment with the wave's queries: every pair is masked
+      const int klo = __builtin_amdgcn_readfirstlane(sSegRange[buf][0]);
+      const int khi = __builtin_amdgcn_readfirstlane(sSegRange[buf][1]);
+      wave_active = wave_active && klo <= qseg_hi && khi >= qseg_lo;
+    }
     if (wave_active) {
       // ---- S^T = K . Q^T : rows = 64 keys (two 32-row blocks), columns = the wave's queries
       f32x16 S[2][NQB];
@@ -317,7 +341,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     // the next tile's copies (issued NS - 2 iterations ago) must have landed; the ones
     // issued this iteration may stay in flight
     if (issue) {
-      store_small(ahead);
+      store_small(ahead, tk0[NS - 1], tke[NS - 1]);
       if constexpr (NS == 3) {
         RA_WAIT_VMCNT(2 * NSEG);
       } else {
