@@ -1,8 +1,10 @@
 """Build libra_attn.so (gfx950) in-tree with hipcc.
 
 Every HIP source under csrc/ is compiled to an object in _build/ and the
-objects are linked into long_context_exact_attn_amd/libra_attn.so.  Packed
-fp32 VALU instructions are disabled for all device code.
+objects are linked into long_context_exact_attn_amd/libra_attn.so.  The
+issue-rate microbenchmark (microbench/rates.hip) is built as a standalone
+program next to its source.  Packed fp32 VALU instructions are disabled for
+all device code.
 """
 import concurrent.futures as cf
 import glob
@@ -42,6 +44,19 @@ def _compile(src, verbose):
     if verbose and noise:
         print("\n".join(noise), file=sys.stderr)
     return obj
+
+
+MICROBENCH = os.path.join(PKG, "microbench", "rates.hip")
+
+
+def build_microbench():
+    """Compile the issue-rate microbenchmark into microbench/rates; returns its path."""
+    exe = os.path.splitext(MICROBENCH)[0]
+    cmd = [hipcc(), *[f for f in common_flags() if f != "-fPIC"], MICROBENCH, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"microbenchmark build failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    return exe
 
 
 def build(verbose=False, jobs=None):

@@ -116,20 +116,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     goff[jj] = row * static_cast<int>(kstride) + chunk * 8;   // < 64 * H * D, checked on the host
     goff0[jj] = chunk * 8;
   }
+  // (raw values are kept until the store, so that the wait for these loads lands there)
   float breg = 0.f;
   int sreg = 0;
+  bool kok = false;
   auto load_small = [&](int64_t key0, int64_t kend) {
     if (tid < BK) {
-      const int64_t key = key0 + tid;
-      if constexpr (HAS_BIAS)
-        breg = key < kend ? p.bias[static_cast<int64_t>(h) * p.bias_len + key % p.bias_len] * kLog2e : 0.f;
-      if constexpr (HAS_SEG) sreg = key < kend ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
+      kok = key0 + tid < kend;
+      const int64_t key = kok ? key0 + tid : key0;
+      if constexpr (HAS_BIAS) breg = p.bias[static_cast<int64_t>(h) * p.bias_len + key % p.bias_len];
+      if constexpr (HAS_SEG) sreg = p.seg[static_cast<int64_t>(b) * p.Lk + key];
     }
   };
   auto store_small = [&](int slot) {
     if (tid < BK) {
-      if constexpr (HAS_BIAS) sBias[slot][tid] = breg;
-      if constexpr (HAS_SEG) sSeg[slot][tid] = sreg;
+      if constexpr (HAS_BIAS) sBias[slot][tid] = kok ? breg * kLog2e : 0.f;
+      if constexpr (HAS_SEG) sSeg[slot][tid] = kok ? sreg : 0;
     }
   };
   auto issue_kv = [&](int64_t key0, int64_t kend, int slot) {
@@ -402,24 +404,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     goff[jj] = row * static_cast<int>(qstride) + chunk * 8;   // < 64 * H * D, checked on the host
     goff0[jj] = chunk * 8;
   }
+  // (raw values are kept until the store, so that the wait for these loads lands there and
+  // not right after them)
   float lreg = 0.f, dreg = 0.f;
   int sreg = 0;
+  bool lok = false;
   auto load_small = [&](int64_t row0, int64_t rend, int64_t pbase) {
     if (tid < BQ) {
       const int64_t r = row0 + tid;
-      const bool ok = r < rend;
-      const int64_t li = (static_cast<int64_t>(b) * p.H + h) * p.Lq + (ok ? r : 0);
-      const float L = p.lse[li];
-      lreg = (ok && L != -INFINITY) ? -L * kLog2e : -INFINITY;
-      dreg = ok ? p.delta[li] : 0.f;
-      if constexpr (HAS_SEG) sreg = ok ? p.seg[static_cast<int64_t>(b) * p.Lk + pbase + r] : 0;
+      lok = r < rend;
+      const int64_t rr = lok ? r : row0;
+      const int64_t li = (static_cast<int64_t>(b) * p.H + h) * p.Lq + rr;
+      lreg = p.lse[li];
+      dreg = p.delta[li];
+      if constexpr (HAS_SEG) sreg = p.seg[static_cast<int64_t>(b) * p.Lk + pbase + rr];
     }
   };
   auto store_small = [&](int slot) {
     if (tid < BQ) {
-      sL[slot][tid] = lreg;
-      sDl[slot][tid] = dreg;
-      if constexpr (HAS_SEG) sSg[slot][tid] = sreg;
+      sL[slot][tid] = (lok && lreg != -INFINITY) ? -lreg * kLog2e : -INFINITY;
+      sDl[slot][tid] = lok ? dreg : 0.f;
+      if constexpr (HAS_SEG) sSg[slot][tid] = lok ? sreg : 0;
     }
   };
   auto issue_qg = [&](int64_t row0, int64_t rend, int slot) {

@@ -143,26 +143,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     goff[j] = row * static_cast<int>(kstride) + chunk * 8;   // < 64 * H * D, checked on the host
     goff0[j] = chunk * 8;
   }
+  // bias / segment ids of the tile (plain loads; the raw values are kept until store_small,
+  // before the barrier, so that the wait for these loads lands there)
   float breg = 0.f;
   int sreg = 0;
-  // bias / segment ids of the tile (plain loads, stored by store_small before the barrier)
+  bool kok = false;
   auto load_small = [&](int64_t key0, int64_t kend) {
     if (tid < BK) {
-      const int64_t key = key0 + tid;
-      if constexpr (HAS_BIAS)
-        breg = key < kend ? p.bias[static_cast<int64_t>(h) * p.bias_len + key % p.bias_len] * kLog2e : 0.f;
-      if constexpr (HAS_SEG) sreg = key < kend ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
+      kok = key0 + tid < kend;
+      const int64_t key = kok ? key0 + tid : key0;
+      if constexpr (HAS_BIAS) breg = p.bias[static_cast<int64_t>(h) * p.bias_len + key % p.bias_len];
+      if constexpr (HAS_SEG) sreg = p.seg[static_cast<int64_t>(b) * p.Lk + key];
     }
   };
-  auto store_small = [&](int slot, int64_t key0, int64_t kend) {
+  auto store_small = [&](int slot) {
     if (tid < BK) {
-      if constexpr (HAS_BIAS) sBias[slot][tid] = breg;
+      if constexpr (HAS_BIAS) sBias[slot][tid] = kok ? breg * kLog2e : 0.f;
       if constexpr (HAS_SEG) {
-        sSeg[slot][tid] = sreg;
+        const int sid = kok ? sreg : 0;
+        sSeg[slot][tid] = sid;
         // the tile's id range lets a wave skip a tile that shares no segment with its queries
-        const bool ok = key0 + tid < kend;
-        const int lo = wave_min_i32(ok ? sreg : INT32_MAX);
-        const int hi = wave_max_i32(ok ? sreg : INT32_MIN);
+        const int lo = wave_min_i32(kok ? sid : INT32_MAX);
+        const int hi = wave_max_i32(kok ? sid : INT32_MIN);
         if (tid == 0) {
           sSegRange[slot][0] = lo;
           sSegRange[slot][1] = hi;
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     if (tok[i]) {
       load_small(tk0[i], tke[i]);
       issue_kv(tk0[i], tke[i], i);
-      store_small(i, tk0[i], tke[i]);
+      store_small(i);
     }
   RA_WAIT_VMCNT(0);
   __syncthreads();
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     // the next tile's copies (issued NS - 2 iterations ago) must have landed; the ones
     // issued this iteration may stay in flight
     if (issue) {
-      store_small(ahead, tk0[NS - 1], tke[NS - 1]);
+      store_small(ahead);
       if constexpr (NS == 3) {
         RA_WAIT_VMCNT(2 * NSEG);
       } else {

@@ -1,0 +1,134 @@
+// Issue-rate microbenchmarks for gfx950, used to set the ceilings the attention kernels are
+// judged against: sustained v_mfma_f32_32x32x16_bf16 throughput, cycles per wave64
+// instruction of v_exp_f32, v_fma_f32, v_dot2_f32_bf16 and v_max, and whether exponentials
+// issued between matrix products of one wave overlap them.  Every thread writes one float
+// of `out` (sized for the largest grid); nothing else is read or written.
+#include <hip/hip_runtime.h>
+#include <cstdio>
+#include <cstdlib>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int N = 4096;
+
+__global__ __launch_bounds__(256) void k_mfma(float* out, float seed) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) { a[i] = (__bf16)(seed * i); b[i] = (__bf16)(seed + i); }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < N; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0; for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+template <int OP>
+__global__ __launch_bounds__(256) void k_valu(float* out, float seed) {
+  float x[8];
+  for (int i = 0; i < 8; ++i) x[i] = seed * (threadIdx.x + i);
+  bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+  for (int it = 0; it < N; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (OP == 0) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+      if (OP == 1) x[i] = __builtin_fmaf(x[i], 0.999f, 0.001f);
+      if (OP == 2) { bf16x2 p = {(__bf16)seed, (__bf16)(seed * 2)}; x[i] = __builtin_amdgcn_fdot2_f32_bf16(p, one, x[i], false); }
+      if (OP == 3) x[i] = fmaxf(fmaxf(x[i], seed), x[(i + 1) & 7]);
+    }
+  }
+  float s = 0; for (int i = 0; i < 8; ++i) s += x[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+// one wave mixes MFMA chains with exp chains: do the pipes overlap?
+template <int NEXP>
+__global__ __launch_bounds__(256) void k_mix(float* out, float seed) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) { a[i] = (__bf16)(seed * i); b[i] = (__bf16)(seed + i); }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  float x[8];
+  for (int i = 0; i < 8; ++i) x[i] = seed * (threadIdx.x + i);
+  for (int it = 0; it < N; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NEXP / 4; ++i) x[i & 7] = __builtin_amdgcn_exp2f(-x[i & 7]);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NEXP / 4; ++i) x[(i + 2) & 7] = __builtin_amdgcn_exp2f(-x[(i + 2) & 7]);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NEXP / 4; ++i) x[(i + 4) & 7] = __builtin_amdgcn_exp2f(-x[(i + 4) & 7]);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NEXP / 4; ++i) x[(i + 6) & 7] = __builtin_amdgcn_exp2f(-x[(i + 6) & 7]);
+  }
+  float s = 0; for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  for (int i = 0; i < 8; ++i) s += x[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+#define CHECK(x)                                                                  \
+  do {                                                                            \
+    hipError_t e_ = (x);                                                          \
+    if (e_ != hipSuccess) {                                                       \
+      fprintf(stderr, "%s failed: %s\n", #x, hipGetErrorString(e_));              \
+      exit(1);                                                                    \
+    }                                                                             \
+  } while (0)
+
+template <typename F>
+float timeit(F f) {
+  hipEvent_t a, b;
+  CHECK(hipEventCreate(&a));
+  CHECK(hipEventCreate(&b));
+  f();
+  CHECK(hipDeviceSynchronize());
+  CHECK(hipEventRecord(a));
+  f();
+  CHECK(hipEventRecord(b));
+  CHECK(hipEventSynchronize(b));
+  float ms;
+  CHECK(hipEventElapsedTime(&ms, a, b));
+  return ms;
+}
+
+int main() {
+  hipDeviceProp_t pr;
+  CHECK(hipGetDeviceProperties(&pr, 0));
+  printf("device %s CUs %d clock %d kHz\n", pr.gcnArchName, pr.multiProcessorCount, pr.clockRate);
+  const int cus = pr.multiProcessorCount;
+  float* out; const int maxwg = cus * 8;
+  CHECK(hipMalloc(&out, sizeof(float) * maxwg * 256));
+  for (int wpc : {1, 2, 4, 8}) {   // workgroups (4 waves each) per CU
+    const int g = cus * wpc;
+    float ms = timeit([&] { hipLaunchKernelGGL(k_mfma, dim3(g), dim3(256), 0, 0, out, 1.0f); });
+    double fl = double(g) * 4 * N * 4 * 32768.0;
+    printf("mfma32x32x16 wg/CU=%d: %.3f ms %.1f TFLOP/s  cycles/mfma/SIMD(at 2.4GHz)=%.2f\n", wpc, ms, fl / ms / 1e9,
+           ms * 1e-3 * 2.4e9 / (double(wpc) * N * 4));
+  }
+  const char* names[] = {"v_exp_f32", "v_fma_f32", "v_dot2_f32_bf16", "v_max(2)"};
+  for (int op = 0; op < 4; ++op)
+    for (int wpc : {1, 2, 4}) {
+      const int g = cus * wpc;
+      float ms = timeit([&] {
+        if (op == 0) hipLaunchKernelGGL(k_valu<0>, dim3(g), dim3(256), 0, 0, out, 0.5f);
+        if (op == 1) hipLaunchKernelGGL(k_valu<1>, dim3(g), dim3(256), 0, 0, out, 0.5f);
+        if (op == 2) hipLaunchKernelGGL(k_valu<2>, dim3(g), dim3(256), 0, 0, out, 0.5f);
+        if (op == 3) hipLaunchKernelGGL(k_valu<3>, dim3(g), dim3(256), 0, 0, out, 0.5f);
+      });
+      double ops = double(g) * 4 * N * 8;   // wave-instructions
+      printf("%s wg/CU=%d: %.3f ms  cycles per wave-instr per SIMD (2.4GHz) = %.2f\n", names[op], wpc, ms,
+             ms * 1e-3 * 2.4e9 * cus * 4 / ops);
+    }
+  for (int wpc : {1, 2}) {
+    const int g = cus * wpc;
+    float m0 = timeit([&] { hipLaunchKernelGGL(k_mix<0>, dim3(g), dim3(256), 0, 0, out, 0.5f); });
+    float m16 = timeit([&] { hipLaunchKernelGGL(k_mix<16>, dim3(g), dim3(256), 0, 0, out, 0.5f); });
+    float m32 = timeit([&] { hipLaunchKernelGGL(k_mix<32>, dim3(g), dim3(256), 0, 0, out, 0.5f); });
+    float m64 = timeit([&] { hipLaunchKernelGGL(k_mix<64>, dim3(g), dim3(256), 0, 0, out, 0.5f); });
+    printf("mix wg/CU=%d (4 mfma + E exp per iter): E=0 %.3f ms, E=16 %.3f, E=32 %.3f, E=64 %.3f\n", wpc, m0, m16, m32, m64);
+  }
+  CHECK(hipFree(out));
+  return 0;
+}
