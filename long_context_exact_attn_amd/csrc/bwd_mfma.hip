@@ -230,6 +230,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
             klim = rel < klim ? static_cast<int>(rel < -1 ? -1 : rel) : klim;
           }
         }
+        // masked scores become -inf (then P = 0) in a pass of their own, so that tiles
+        // without masks run the loop below with no selects
+        if (need_mask) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int kr = mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+              bool vis = kr <= klim;
+              if constexpr (HAS_SEG) vis = vis && kseg[mb][v] == qseg[nb];
+              S[mb][nb][v] = vis ? S[mb][nb][v] : -INFINITY;
+            }
+        }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -239,13 +252,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
             for (int i = 0; i < 8; ++i) {
               const int v = 8 * st + i;
               const int kr = mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-              float y = HAS_BIAS ? __builtin_fmaf(S[mb][nb][v], c, sBias[buf][kr] - lse2[nb])
-                                 : __builtin_fmaf(S[mb][nb][v], c, -lse2[nb]);
-              if (need_mask) {
-                bool vis = kr <= klim;
-                if constexpr (HAS_SEG) vis = vis && kseg[mb][v] == qseg[nb];
-                y = vis ? y : -INFINITY;
-              }
+              const float y = HAS_BIAS ? __builtin_fmaf(S[mb][nb][v], c, sBias[buf][kr] - lse2[nb])
+                                       : __builtin_fmaf(S[mb][nb][v], c, -lse2[nb]);
               const float pr = __builtin_amdgcn_exp2f(y);
               e[i] = pr * (G[mb][nb][v] - dlt[nb]);
             }
@@ -308,7 +316,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 }
 
 // ================================================================== dK/dV (K/V tiles stationary)
-constexpr int kBqKv = 64;   // queries per LDS tile
+#ifndef RA_KV_BQ
+#define RA_KV_BQ 64
+#endif
+constexpr int kBqKv = RA_KV_BQ;   // queries per LDS tile
 
 template <int D, int NKB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void dkdv_mfma_kernel(Params p) {
@@ -324,7 +335,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   constexpr int TILE = BQ * D;         // unpadded, swizzled
   constexpr int NSEG = TILE * 2 / 1024 / kWaves;   // 1 KiB direct-copy segments per wave per tile
   static_assert(NSEG * 1024 * kWaves == TILE * 2, "tile must split into 1 KiB segments");
-  static_assert(BQ == 64, "two 32-query blocks per tile");
+  static_assert(BQ % 32 == 0 && BQ <= kThreads, "whole 32-query blocks per tile");
 
   __shared__ __attribute__((aligned(16))) __bf16 sQ[NS][TILE];
   __shared__ __attribute__((aligned(16))) __bf16 sG[NS][TILE];
@@ -488,7 +499,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         krel[kb] = rel < 0 ? 0 : (rel > BQ ? BQ : static_cast<int>(rel));
       }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < BQ / 32; ++qb) {
         f32x16 S[NKB], G[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -526,6 +537,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
             qs[4 * g4 + 3] = z.w;
           }
         }
+        // masked scores become -inf (then P = 0) in a pass of their own, so that tiles
+        // without masks run the loop below with no selects
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int qr = qb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+              bool vis = true;
+              if constexpr (CAUSAL) vis = krel[kb] <= qr;
+              if constexpr (HAS_SEG) vis = vis && ksg[kb] == qs[v];
+              S[kb][v] = vis ? S[kb][v] : -INFINITY;
+            }
+        }
         bf16x8 Pb[NKB][2], Sb[NKB][2];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -535,14 +560,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
               const int v = 8 * st + i;
-              const int qr = qb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-              float y = HAS_BIAS ? __builtin_fmaf(S[kb][v], c, kbias[kb] + nl[v]) : __builtin_fmaf(S[kb][v], c, nl[v]);
-              if (need_mask) {
-                bool vis = true;
-                if constexpr (CAUSAL) vis = krel[kb] <= qr;
-                if constexpr (HAS_SEG) vis = vis && ksg[kb] == qs[v];
-                y = vis ? y : -INFINITY;
-              }
+              const float y = HAS_BIAS ? __builtin_fmaf(S[kb][v], c, kbias[kb] + nl[v]) : __builtin_fmaf(S[kb][v], c, nl[v]);
               const float pr = __builtin_amdgcn_exp2f(y);
               pe[i] = pr;
               de[i] = pr * (G[kb][v] - dl[v]);
