@@ -134,6 +134,43 @@ int ra_blockwise_attn_bwd_dq(const void* q, const void* k, const void* v, const 
                              int32_t causal, const float* lse, const float* delta, const void* dout, void* dq,
                              const ra_shape* shape, void* stream);
 
+/*
+ * One ring step of the forward pass, for use inside a real ring where the K/V blocks arrive one
+ * at a time ("手把手拆解RingAttention", section 2: each device works on the key/value block it
+ * holds while that block moves on to the next device).  The queries q [B,Lq,H,D] sit at global
+ * positions q_pos0 + i; the block k, v [B,Lk,H,D] (Lk == Lq: ring blocks are equal) holds the
+ * keys at global positions kv_pos0 + j.  The call folds that block into the running state with
+ * the online-softmax merge (the reading of the pages' "complete attention map", section 1):
+ *   o_state [B,Lq,H,D] float32: unnormalised accumulator;
+ *   m_state [B,H,Lq] float32: reference row maximum in log2 units (score * log2 e);
+ *   l_state [B,H,Lq] float32: sum of exponentials against m_state.
+ * init = 1 starts from the empty state (the incoming state is not read); otherwise the state
+ * left by the previous step is read and updated in place.  The masks, bias and scale are those
+ * of ra_blockwise_attn_fwd, on global positions: causal compares kv_pos0 + j with q_pos0 + i,
+ * bias is read at key position kv_pos0 + j, and segment_ids [B, seg_len] (seg_len covering
+ * both blocks' positions) are indexed by global position.  shape.ring_rank is ignored;
+ * shape.q_len == shape.kv_len is the block length.  Blocks may come in any order; after the
+ * last step ra_blockwise_attn_fwd_finalize gives out and lse.  RA_BF16 only.
+ */
+int ra_blockwise_attn_fwd_step(const void* q, const void* k, const void* v, const float* bias,
+                               const int32_t* segment_ids, int64_t seg_len, int64_t q_pos0, int64_t kv_pos0,
+                               int32_t causal, float* o_state, float* m_state, float* l_state, int32_t init,
+                               const ra_shape* shape, void* stream);
+
+/* out [B,Lq,H,D] (dtype) = o_state / l_state and lse [B,H,Lq] = natural log of l_state plus the
+ * reference maximum: the forward's outputs from the state of the last ring step (rows that saw no
+ * visible key: out 0, lse -inf).  shape gives B, H, D, Lq (= q_len) and the dtype of out. */
+int ra_blockwise_attn_fwd_finalize(const float* o_state, const float* m_state, const float* l_state, void* out,
+                                   float* lse, const ra_shape* shape, void* stream);
+
+/* Merge of two partial attentions of the same queries over disjoint key sets (for instance two
+ * halves of the ring computed separately): with lse = log(exp(lse_a) + exp(lse_b)),
+ *   out_a <- exp(lse_a - lse) out_a + exp(lse_b - lse) out_b,   lse_a <- lse   (in place).
+ * out_a, out_b [B,Lq,H,D] (dtype), lse_a, lse_b [B,H,Lq] float32; shape gives B, H, D, Lq and the
+ * dtype.  This is the online-softmax merge rule applied to normalised partial results. */
+int ra_attn_merge(void* out_a, float* lse_a, const void* out_b, const float* lse_b, const ra_shape* shape,
+                  void* stream);
+
 /* Description of the last error on the calling thread ("" after a success). */
 const char* ra_last_error(void);
 

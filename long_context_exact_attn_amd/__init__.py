@@ -13,6 +13,9 @@ from .api import (  # noqa: F401
     blockwise_attn_bwd_preprocess,
     blockwise_attn_bwd_dkdv,
     blockwise_attn_bwd_dq,
+    blockwise_attn_fwd_step,
+    blockwise_attn_fwd_finalize,
+    attn_merge,
     bwd_workspace_size,
     library_path,
     load_library,

@@ -54,6 +54,9 @@ def load_library():
         "ra_blockwise_attn_bwd_preprocess": [P, P, P, SH, P],
         "ra_blockwise_attn_bwd_dkdv": [P, P, P, P, P, I32, I64, I64, I32, P, P, P, P, P, SH, P],
         "ra_blockwise_attn_bwd_dq": [P, P, P, P, P, I32, I64, I64, I32, P, P, P, P, SH, P],
+        "ra_blockwise_attn_fwd_step": [P, P, P, P, P, I64, I64, I64, I32, P, P, P, I32, SH, P],
+        "ra_blockwise_attn_fwd_finalize": [P, P, P, P, P, SH, P],
+        "ra_attn_merge": [P, P, P, P, SH, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -192,6 +195,63 @@ def blockwise_attn_bwd_dq(q, k, v, lse, delta, dout, bias=None, segment_ids=None
                                         int(q_chunk), int(k_chunk), int(bool(causal)), _ptr(lse), _ptr(delta),
                                         _ptr(dout), _ptr(dq), ctypes.byref(shape), _stream(q.device)))
     return dq
+
+
+def blockwise_attn_fwd_step(q, k, v, bias=None, segment_ids=None, *, q_pos0, kv_pos0, causal, state=None,
+                            init=None, scale=None):
+    """One ring step (ra_blockwise_attn_fwd_step): fold the K/V block held (keys at global positions
+    kv_pos0 + j) into the running state of the queries q (global positions q_pos0 + i).
+
+    state is (o, m, l) from the previous step, updated in place; None allocates a new one.  init
+    (default: state is None) makes the step ignore what the state holds and start afresh.
+    segment_ids, when given, is int32 [batch, seg_len] on global positions.  Returns the state."""
+    lib = load_library()
+    _tensors(q, k, v, bias, None)
+    if segment_ids is not None and (segment_ids.dtype != torch.int32 or segment_ids.dim() != 2
+                                    or segment_ids.shape[0] != q.shape[0] or not segment_ids.is_cuda
+                                    or not segment_ids.is_contiguous()):
+        raise ValueError("segment_ids must be a contiguous int32 GPU tensor of shape [batch, seq_len]")
+    B, Lq, H, D = q.shape
+    init = state is None if init is None else bool(init)
+    if state is None:
+        state = (torch.empty((B, Lq, H, D), dtype=torch.float32, device=q.device),
+                 torch.empty((B, H, Lq), dtype=torch.float32, device=q.device),
+                 torch.empty((B, H, Lq), dtype=torch.float32, device=q.device))
+    o, m, l_ = state
+    _tensors(q, k, v, None, None, extra=(("o", o), ("m", m), ("l", l_)))
+    shape = make_shape(q, k, ring_rank=0, scale=scale, bias=bias)
+    seg_len = 0 if segment_ids is None else segment_ids.shape[1]
+    _check(lib.ra_blockwise_attn_fwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(seg_len),
+                                          int(q_pos0), int(kv_pos0), int(bool(causal)), _ptr(o), _ptr(m), _ptr(l_),
+                                          int(init), ctypes.byref(shape), _stream(q.device)))
+    return state
+
+
+def blockwise_attn_fwd_finalize(state, *, dtype=torch.bfloat16, out=None, lse=None):
+    """out, lse = ra_blockwise_attn_fwd_finalize(state) after the last ring step."""
+    lib = load_library()
+    o, m, l_ = state
+    B, Lq, H, D = o.shape
+    out = torch.empty((B, Lq, H, D), dtype=dtype, device=o.device) if out is None else out
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=o.device) if lse is None else lse
+    _tensors(o, o, o, None, None, extra=(("m", m), ("l", l_), ("out", out), ("lse", lse)))
+    shape = Shape(B, H, D, -1, Lq, Lq, 0, 0.0, _DTYPES[dtype])
+    _check(lib.ra_blockwise_attn_fwd_finalize(_ptr(o), _ptr(m), _ptr(l_), _ptr(out), _ptr(lse), ctypes.byref(shape),
+                                              _stream(o.device)))
+    return out, lse
+
+
+def attn_merge(out_a, lse_a, out_b, lse_b):
+    """ra_attn_merge: fold (out_b, lse_b) into (out_a, lse_a) in place; returns out_a, lse_a."""
+    lib = load_library()
+    _tensors(out_a, out_a, out_a, None, None, extra=(("lse_a", lse_a), ("out_b", out_b), ("lse_b", lse_b)))
+    if out_b.shape != out_a.shape or out_b.dtype != out_a.dtype or lse_b.shape != lse_a.shape:
+        raise ValueError("the two partial results must have the same shapes and dtype")
+    B, Lq, H, D = out_a.shape
+    shape = Shape(B, H, D, -1, Lq, Lq, 0, 0.0, _DTYPES[out_a.dtype])
+    _check(lib.ra_attn_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), ctypes.byref(shape),
+                             _stream(out_a.device)))
+    return out_a, lse_a
 
 
 def default_scale(head_dim):

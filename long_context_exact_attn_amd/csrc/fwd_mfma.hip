@@ -39,7 +39,9 @@ struct FwdLds {
 
 // OCC: waves per SIMD the register allocation must allow (2 lets one wave's softmax
 // arithmetic run while the other's matrix products do).
-template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC>
+// STEP: one ring step (see ra_blockwise_attn_fwd_step): the keys held are one block at global
+// positions kv_pos0 + j, the running state is read from and written back to caller memory.
+template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC, bool STEP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_mfma_kernel(Params p) {
   constexpr int QW = 32 * NQB;         // queries per wave
   constexpr int BQ = kWaves * QW;      // queries per workgroup
@@ -76,7 +78,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   const int64_t qa = (t % n_qt_blk) * BQ;                  // first row of the tile inside its block
   const int r = p.ring_rank < 0 ? r_local : p.ring_rank;
   const int64_t qrow_base = static_cast<int64_t>(r_local) * p.Lb;   // local row of the block's row 0
-  const int64_t pos0 = static_cast<int64_t>(r) * p.Lb + qa;         // global position of the tile's row 0
+  // position of the tile's row 0 in the coordinates of the keys held (global positions minus
+  // kv_pos0, which is 0 outside a single ring step)
+  const int64_t pos0 = (STEP ? p.q_pos0 - p.kv_pos0 : static_cast<int64_t>(r) * p.Lb) + qa;
   const int64_t nrows = (p.Lb - qa) < BQ ? (p.Lb - qa) : BQ;
 
   const __bf16* __restrict__ qp = static_cast<const __bf16*>(p.q);
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     for (int nb = 0; nb < NQB; ++nb) {
       int64_t pos = wpos0 + nb * 32 + l32;
       const bool ok = wrow0 + nb * 32 + l32 < p.Lb;
-      qseg[nb] = ok ? p.seg[static_cast<int64_t>(b) * p.Lk + pos] : 0;
+      qseg[nb] = ok ? p.seg[static_cast<int64_t>(b) * p.seg_len + p.kv_pos0 + pos] : 0;
       lo = ok ? min(lo, qseg[nb]) : lo;
       hi = ok ? max(hi, qseg[nb]) : hi;
     }
@@ -124,6 +128,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     lsum[nb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) O[db][nb] = f32x16{};
+  }
+
+  if constexpr (STEP) {
+    if (!p.step_init) {
+      // the running state of an earlier ring step: O^T fragments as stored by the epilogue,
+      // m (log2 units) in both lanes of a column, l in the lower one (the pair sums to it)
+#pragma unroll
+      for (int nb = 0; nb < NQB; ++nb) {
+        const int64_t row = wrow0 + nb * 32 + l32;
+        if (row >= p.Lb) continue;
+        const float* src = p.o_state + row_offset(b, row, h, p.Lq, p.H, D);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(src + db * 32 + 8 * v4 + 4 * hh);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[db][nb][4 * v4 + i] = x[i];
+          }
+        const int64_t si = (static_cast<int64_t>(b) * p.H + h) * p.Lq + row;
+        m[nb] = p.m_state[si];
+        lsum[nb] = hh == 0 ? p.l_state[si] : 0.f;
+      }
+    }
   }
 
   // ---- K/V tile staging: direct global -> LDS copies into a ring of NS stages, issued
@@ -152,8 +180,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     if (tid < BK) {
       kok = key0 + tid < kend;
       const int64_t key = kok ? key0 + tid : key0;
-      if constexpr (HAS_BIAS) breg = p.bias[static_cast<int64_t>(h) * p.bias_len + key % p.bias_len];
-      if constexpr (HAS_SEG) sreg = p.seg[static_cast<int64_t>(b) * p.Lk + key];
+      if constexpr (HAS_BIAS) breg = p.bias[static_cast<int64_t>(h) * p.bias_len + (p.kv_pos0 + key) % p.bias_len];
+      if constexpr (HAS_SEG) sreg = p.seg[static_cast<int64_t>(b) * p.seg_len + p.kv_pos0 + key];
     }
   };
   auto store_small = [&](int slot) {
@@ -365,6 +393,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     tke[NS - 1] = walk.kend;
   }
 
+  if constexpr (STEP) {
+    // ---- epilogue of a ring step: the running state goes back to caller memory
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+      const int64_t row = wrow0 + nb * 32 + l32;
+      const float lt = pair_sum(lsum[nb]);
+      if (row >= p.Lb) continue;
+      float* dst = p.o_state + row_offset(b, row, h, p.Lq, p.H, D);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          f32x4 x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = O[db][nb][4 * v4 + i];
+          *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * v4 + 4 * hh) = x;
+        }
+      if (hh == 0) {
+        const int64_t si = (static_cast<int64_t>(b) * p.H + h) * p.Lq + row;
+        p.m_state[si] = m[nb];
+        p.l_state[si] = lt;
+      }
+    }
+    return;
+  }
   // ---- epilogue: out = O / l, lse = m + log l (natural log)
   __bf16* __restrict__ op = static_cast<__bf16*>(p.out);
 #pragma unroll
@@ -389,7 +442,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   }
 }
 
-template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
+template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, bool STEP>
 hipError_t launch_t(const Params& p, hipStream_t st) {
   constexpr int BQ = kWaves * 32 * NQB;
   const int64_t n_qt = (p.ring_rank < 0 ? p.n_ring : 1) * ((p.Lb + BQ - 1) / BQ);
@@ -398,27 +451,33 @@ hipError_t launch_t(const Params& p, hipStream_t st) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   // segment ids cost registers: those variants keep one wave per SIMD rather than spill
   constexpr int OCC = (HAS_SEG || (HAS_BIAS && D == 64)) ? 1 : 2;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, NQB, CAUSAL, HAS_BIAS, HAS_SEG, OCC>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, NQB, CAUSAL, HAS_BIAS, HAS_SEG, OCC, STEP>), dim3(static_cast<unsigned>(grid)),
                      dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
-template <int D, int NQB>
+template <int D, int NQB, bool STEP>
 hipError_t launch_d(const Params& p, hipStream_t st) {
   const bool c = p.causal != 0, bi = p.bias != nullptr, sg = p.seg != nullptr;
   if (c) {
-    if (bi) return sg ? launch_t<D, NQB, true, true, true>(p, st) : launch_t<D, NQB, true, true, false>(p, st);
-    return sg ? launch_t<D, NQB, true, false, true>(p, st) : launch_t<D, NQB, true, false, false>(p, st);
+    if (bi) return sg ? launch_t<D, NQB, true, true, true, STEP>(p, st) : launch_t<D, NQB, true, true, false, STEP>(p, st);
+    return sg ? launch_t<D, NQB, true, false, true, STEP>(p, st) : launch_t<D, NQB, true, false, false, STEP>(p, st);
   }
-  if (bi) return sg ? launch_t<D, NQB, false, true, true>(p, st) : launch_t<D, NQB, false, true, false>(p, st);
-  return sg ? launch_t<D, NQB, false, false, true>(p, st) : launch_t<D, NQB, false, false, false>(p, st);
+  if (bi) return sg ? launch_t<D, NQB, false, true, true, STEP>(p, st) : launch_t<D, NQB, false, true, false, STEP>(p, st);
+  return sg ? launch_t<D, NQB, false, false, true, STEP>(p, st) : launch_t<D, NQB, false, false, false, STEP>(p, st);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_mfma(const Params& p, hipStream_t st) {
-  if (p.D == 64) return launch_d<64, 2>(p, st);
-  if (p.D == 128) return launch_d<128, 1>(p, st);
+  if (p.D == 64) return launch_d<64, 2, false>(p, st);
+  if (p.D == 128) return launch_d<128, 1, false>(p, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_step_mfma(const Params& p, hipStream_t st) {
+  if (p.D == 64) return launch_d<64, 2, true>(p, st);
+  if (p.D == 128) return launch_d<128, 1, true>(p, st);
   return hipErrorInvalidValue;
 }
 

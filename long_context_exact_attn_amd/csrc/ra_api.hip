@@ -78,6 +78,7 @@ int check_shape(const ra_shape* s, int32_t n_ring, Checked* c) {
   p = ra::Params{};
   p.Lq = s->q_len;
   p.Lk = s->kv_len;
+  p.seg_len = s->kv_len;
   p.Lb = Lb;
   p.bias_len = s->bias_len;
   p.B = s->batch;
@@ -284,6 +285,98 @@ int ra_blockwise_attn_bwd(const void* q, const void* k, const void* v, const flo
   if (c.kv_elems > 0) RA_TRY(do_bwd_dkdv(c, st));
   if (c.rows > 0) RA_TRY(do_bwd_dq(c, st));
   return ok();
+}
+
+int ra_blockwise_attn_fwd_step(const void* q, const void* k, const void* v, const float* bias,
+                               const int32_t* segment_ids, int64_t seg_len, int64_t q_pos0, int64_t kv_pos0,
+                               int32_t causal, float* o_state, float* m_state, float* l_state, int32_t init,
+                               const ra_shape* shape, void* stream) {
+  RA_TRY(check_dims(shape));
+  if (shape->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "ring steps are implemented for RA_BF16 only");
+  if (shape->q_len != shape->kv_len)
+    return fail(RA_ERR_SHAPE, "a ring step needs equal query and key blocks (q_len %lld, kv_len %lld)",
+                (long long)shape->q_len, (long long)shape->kv_len);
+  if (q_pos0 < 0 || kv_pos0 < 0) return fail(RA_ERR_ARG, "q_pos0 and kv_pos0 must be >= 0");
+  if (init != 0 && init != 1) return fail(RA_ERR_ARG, "init must be 0 or 1 (got %d)", init);
+  ra_shape blk = *shape;
+  blk.ring_rank = 0;   // one block: the walk visits the keys held, causal on the global positions below
+  Checked c;
+  RA_TRY(check_shape(&blk, 1, &c));
+  RA_TRY(check_mask_args(&blk, bias, 1, 1, causal, &c));
+  RA_TRY(check_inputs(c, q, k, v, bias, segment_ids, &blk));
+  if (segment_ids) {
+    const int64_t need = (q_pos0 > kv_pos0 ? q_pos0 : kv_pos0) + shape->q_len;
+    if (seg_len < need)
+      return fail(RA_ERR_SHAPE, "segment_ids rows of %lld positions do not cover position %lld", (long long)seg_len,
+                  (long long)(need - 1));
+  }
+  RA_TRY(need_ptr(o_state, c.q_elems, "o_state", 16));
+  RA_TRY(need_ptr(m_state, c.rows, "m_state", 4));
+  RA_TRY(need_ptr(l_state, c.rows, "l_state", 4));
+  if (c.rows == 0) return ok();
+  c.p.q = q;
+  c.p.k = k;
+  c.p.v = v;
+  c.p.bias = bias;
+  c.p.seg = segment_ids;
+  c.p.seg_len = segment_ids ? seg_len : blk.kv_len;
+  c.p.q_pos0 = q_pos0;
+  c.p.kv_pos0 = kv_pos0;
+  c.p.o_state = o_state;
+  c.p.m_state = m_state;
+  c.p.l_state = l_state;
+  c.p.step_init = init;
+  return hip_status(ra::launch_fwd_step_mfma(c.p, static_cast<hipStream_t>(stream)), "ring step launch");
+}
+
+int ra_blockwise_attn_fwd_finalize(const float* o_state, const float* m_state, const float* l_state, void* out,
+                                   float* lse, const ra_shape* shape, void* stream) {
+  RA_TRY(check_dims(shape));
+  Checked c;
+  c.p = ra::Params{};
+  c.p.B = shape->batch;
+  c.p.H = shape->heads;
+  c.p.D = shape->head_dim;
+  c.p.Lq = shape->q_len;
+  c.p.bf16 = shape->dtype == RA_BF16;
+  c.rows = static_cast<int64_t>(shape->batch) * shape->heads * shape->q_len;
+  c.q_elems = c.rows * shape->head_dim;
+  if ((c.rows + 255) / 256 > 0x7fffffffLL) return fail(RA_ERR_SHAPE, "problem too large for one launch");
+  RA_TRY(need_ptr(o_state, c.q_elems, "o_state", 16));
+  RA_TRY(need_ptr(m_state, c.rows, "m_state", 4));
+  RA_TRY(need_ptr(l_state, c.rows, "l_state", 4));
+  RA_TRY(need_ptr(out, c.q_elems, "out", 16));
+  RA_TRY(need_ptr(lse, c.rows, "lse", 4));
+  if (c.rows == 0) return ok();
+  c.p.o_state = const_cast<float*>(o_state);
+  c.p.m_state = const_cast<float*>(m_state);
+  c.p.l_state = const_cast<float*>(l_state);
+  c.p.out = out;
+  c.p.lse = lse;
+  return hip_status(ra::launch_fwd_finalize(c.p, static_cast<hipStream_t>(stream)), "finalize launch");
+}
+
+int ra_attn_merge(void* out_a, float* lse_a, const void* out_b, const float* lse_b, const ra_shape* shape,
+                  void* stream) {
+  RA_TRY(check_dims(shape));
+  Checked c;
+  c.p = ra::Params{};
+  c.p.B = shape->batch;
+  c.p.H = shape->heads;
+  c.p.D = shape->head_dim;
+  c.p.Lq = shape->q_len;
+  c.p.bf16 = shape->dtype == RA_BF16;
+  c.rows = static_cast<int64_t>(shape->batch) * shape->heads * shape->q_len;
+  c.q_elems = c.rows * shape->head_dim;
+  if ((c.rows + 255) / 256 > 0x7fffffffLL) return fail(RA_ERR_SHAPE, "problem too large for one launch");
+  RA_TRY(need_ptr(out_a, c.q_elems, "out_a", 16));
+  RA_TRY(need_ptr(lse_a, c.rows, "lse_a", 4));
+  RA_TRY(need_ptr(out_b, c.q_elems, "out_b", 16));
+  RA_TRY(need_ptr(lse_b, c.rows, "lse_b", 4));
+  if (c.rows == 0) return ok();
+  c.p.out = out_a;
+  c.p.lse = lse_a;
+  return hip_status(ra::launch_merge(c.p, out_b, lse_b, static_cast<hipStream_t>(stream)), "merge launch");
 }
 
 }  // extern "C"

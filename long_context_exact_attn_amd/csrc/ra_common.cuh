@@ -45,6 +45,13 @@ struct Params {
   int32_t B, H, D, n_ring, ring_rank, causal;
   int32_t bf16;             // 1: bfloat16 tensors, 0: float32
   float scale;              // resolved (> 0)
+  // one ring step (ra_blockwise_attn_fwd_step): the keys held are global positions
+  // kv_pos0 + j, the queries q_pos0 + i; segment ids are [B, seg_len] on global positions
+  int64_t q_pos0, kv_pos0, seg_len;
+  float* o_state;           // [B, Lq, H, D] unnormalised accumulator
+  float* m_state;           // [B, H, Lq] reference maximum, log2 units
+  float* l_state;           // [B, H, Lq] sum of exponentials against m_state
+  int32_t step_init;        // 1: start from an empty state (the incoming one is not read)
 };
 
 // ---------------------------------------------------------------- element access
@@ -134,6 +141,9 @@ struct QueryWalk {
 
 // ---------------------------------------------------------------- launchers (validated Params only)
 hipError_t launch_fwd_mfma(const Params& p, hipStream_t st);
+hipError_t launch_fwd_step_mfma(const Params& p, hipStream_t st);
+hipError_t launch_fwd_finalize(const Params& p, hipStream_t st);
+hipError_t launch_merge(const Params& p, const void* out_b, const float* lse_b, hipStream_t st);
 hipError_t launch_fwd_simt(const Params& p, hipStream_t st);
 hipError_t launch_bwd_preprocess(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dkdv_simt(const Params& p, hipStream_t st);

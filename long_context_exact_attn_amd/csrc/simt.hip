@@ -139,6 +139,59 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(Params p) {
   p.delta_out[(static_cast<int64_t>(b) * p.H + h) * p.Lq + i] = acc;
 }
 
+// ------------------------------------------------------------------ ring-step finalize and merge
+// One lane per (b, i, h) row.  finalize: out = O / l, lse = (m + log2 l) ln 2 from the running state
+// of ra_blockwise_attn_fwd_step (m in log2 units).  merge: the attention over the union of two
+// disjoint key sets from the attention over each,
+//   lse = log(exp(lse_a) + exp(lse_b)),  out = exp(lse_a - lse) out_a + exp(lse_b - lse) out_b.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void finalize_kernel(Params p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;   // (b, i, h) in memory order
+  const int64_t rows = static_cast<int64_t>(p.B) * p.Lq * p.H;
+  if (idx >= rows) return;
+  const int h = static_cast<int>(idx % p.H);
+  const int64_t i = (idx / p.H) % p.Lq;
+  const int b = static_cast<int>(idx / (static_cast<int64_t>(p.H) * p.Lq));
+  const int64_t si = (static_cast<int64_t>(b) * p.H + h) * p.Lq + i;
+  const float l = p.l_state[si];
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float* o = p.o_state + idx * D;
+  T* dst = static_cast<T*>(p.out) + idx * D;
+#pragma unroll
+  for (int d = 0; d < D; d += 4) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(o + d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[d + e] = from_f32<T>(x[e] * inv);
+  }
+  p.lse[si] = l > 0.f ? (p.m_state[si] + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(Params p, const T* out_b, const float* lse_b) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t rows = static_cast<int64_t>(p.B) * p.Lq * p.H;
+  if (idx >= rows) return;
+  const int h = static_cast<int>(idx % p.H);
+  const int64_t i = (idx / p.H) % p.Lq;
+  const int b = static_cast<int>(idx / (static_cast<int64_t>(p.H) * p.Lq));
+  const int64_t si = (static_cast<int64_t>(b) * p.H + h) * p.Lq + i;
+  const float la = p.lse[si], lb = lse_b[si];     // p.lse / p.out: the first pair, also the result
+  const float mx = fmaxf(la, lb);
+  float wa = 0.f, wb = 0.f, lse = -INFINITY;
+  if (mx != -INFINITY) {
+    wa = __builtin_amdgcn_exp2f((la - mx) * kLog2e);
+    wb = __builtin_amdgcn_exp2f((lb - mx) * kLog2e);
+    const float sum = wa + wb;
+    lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+    wa /= sum;
+    wb /= sum;
+  }
+  T* oa = static_cast<T*>(p.out) + idx * D;
+  const T* ob = out_b + idx * D;
+  for (int d = 0; d < D; ++d) oa[d] = from_f32<T>(wa * to_f32(oa[d]) + wb * to_f32(ob[d]));
+  p.lse[si] = lse;
+}
+
 // ------------------------------------------------------------------ backward dK/dV (one lane per key)
 template <typename T, int D, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
 __global__ __launch_bounds__(kLanes) void dkdv_simt_kernel(Params p) {
@@ -390,6 +443,34 @@ hipError_t launch_bwd_dq_simt_t(const Params& p, hipStream_t st) {
   if (p.D == 128) return dq_simt_d<T, 128>(p, st);
   return hipErrorInvalidValue;
 }
+template <typename T>
+hipError_t launch_finalize_t(const Params& p, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(p.B) * p.Lq * p.H;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((rows + 255) / 256));
+  if (p.D == 64) hipLaunchKernelGGL((finalize_kernel<T, 64>), grid, dim3(256), 0, st, p);
+  else if (p.D == 128) hipLaunchKernelGGL((finalize_kernel<T, 128>), grid, dim3(256), 0, st, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+template <typename T>
+hipError_t launch_merge_t(const Params& p, const void* out_b, const float* lse_b, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(p.B) * p.Lq * p.H;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((rows + 255) / 256));
+  const T* ob = static_cast<const T*>(out_b);
+  if (p.D == 64) hipLaunchKernelGGL((merge_kernel<T, 64>), grid, dim3(256), 0, st, p, ob, lse_b);
+  else if (p.D == 128) hipLaunchKernelGGL((merge_kernel<T, 128>), grid, dim3(256), 0, st, p, ob, lse_b);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+hipError_t launch_fwd_finalize(const Params& p, hipStream_t st) {
+  return p.bf16 ? launch_finalize_t<__bf16>(p, st) : launch_finalize_t<float>(p, st);
+}
+hipError_t launch_merge(const Params& p, const void* out_b, const float* lse_b, hipStream_t st) {
+  return p.bf16 ? launch_merge_t<__bf16>(p, out_b, lse_b, st) : launch_merge_t<float>(p, out_b, lse_b, st);
+}
+
 hipError_t launch_bwd_preprocess(const Params& p, hipStream_t st) {
   return p.bf16 ? launch_bwd_preprocess_t<__bf16>(p, st) : launch_bwd_preprocess_t<float>(p, st);
 }

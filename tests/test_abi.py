@@ -143,3 +143,35 @@ def test_empty_problem_is_a_no_op():
     s = api.Shape(0, 2, 64, -1, 1024, 1024, 0, 0.0, api.RA_BF16)   # batch 0: nothing to do, NULLs allowed
     assert _fwd(lib, s, q=None, k=None, v=None) == 0
     assert lib.ra_last_error() == b""
+
+
+@needs_cpu
+def test_ring_step_validation():
+    lib = _lib()
+    S = lambda **kw: api.Shape(**{**dict(batch=1, heads=2, head_dim=64, ring_rank=-1, q_len=512, kv_len=512,  # noqa
+                                         bias_len=0, scale=0.0, dtype=api.RA_BF16), **kw})
+
+    def step(shape, seg=None, seg_len=0, q_pos0=512, kv_pos0=0, init=1, o=None, m=FAKE, l_=FAKE, causal=1):
+        return lib.ra_blockwise_attn_fwd_step(FAKE, FAKE, FAKE, None, seg, seg_len, q_pos0, kv_pos0, causal, o, m,
+                                              l_, init, ctypes.byref(shape), None)
+
+    # o_state stays NULL in every call: none can reach a launch
+    assert step(S(kv_len=256)) == -2 and b"equal query and key" in lib.ra_last_error()
+    assert step(S(dtype=api.RA_F32)) == -3
+    assert step(S(head_dim=80)) == -3
+    assert step(S(), q_pos0=-1) == -1
+    assert step(S(), init=2) == -1
+    assert step(S(), causal=3) == -1
+    assert step(S(), seg=FAKE, seg_len=1000) == -2 and b"do not cover" in lib.ra_last_error()
+    assert step(S()) == -1 and b"o_state" in lib.ra_last_error()
+    assert step(S(batch=0), m=None, l_=None) == 0   # nothing to do
+
+    s = S()
+    rc = lib.ra_blockwise_attn_fwd_finalize(FAKE, FAKE, FAKE, FAKE, None, ctypes.byref(s), None)
+    assert rc == -1 and b"lse" in lib.ra_last_error()
+    rc = lib.ra_blockwise_attn_fwd_finalize(FAKE, FAKE, FAKE, None, FAKE, ctypes.byref(S(head_dim=32)), None)
+    assert rc == -3
+    rc = lib.ra_attn_merge(FAKE, FAKE, FAKE, None, ctypes.byref(s), None)
+    assert rc == -1 and b"lse_b" in lib.ra_last_error()
+    rc = lib.ra_attn_merge(None, FAKE, FAKE, FAKE, ctypes.byref(S(batch=-2)), None)
+    assert rc == -2

@@ -1,0 +1,151 @@
+"""GPU parity of the per-ring-step entry points: a chain of ra_blockwise_attn_fwd_step calls,
+one per K/V block in ring order, then ra_blockwise_attn_fwd_finalize, must give the oracle's
+attention of the device's query block over the whole sequence; ra_attn_merge of two partial
+results over disjoint key blocks must give the same ("手把手拆解RingAttention", sections 1-2:
+a device keeps its query block while K/V blocks pass it, one per step)."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_exact_attn_amd as ra
+from long_context_exact_attn_amd import workloads as W
+import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _block(x, j, lb):
+    return x[:, j * lb:(j + 1) * lb].contiguous()
+
+
+def _chain(w, t, blocks, state=None, init=None):
+    lb, r = w.block_len, w.ring_rank
+    for s, j in enumerate(blocks):
+        state = ra.blockwise_attn_fwd_step(t["q"], _block(t["k"], j, lb), _block(t["v"], j, lb), t["bias"],
+                                           t["segment_ids"], q_pos0=r * lb, kv_pos0=j * lb, causal=w.causal,
+                                           state=state, init=init if s == 0 else False)
+    return state
+
+
+def _ring_order(w):
+    n, r = w.n_ring, w.ring_rank
+    return [(r - s) % n for s in range(n)]
+
+
+def _oracle(w, t):
+    d = P.oracle_inputs(t)
+    return P.oracle_forward(w, d, w.q_positions())
+
+
+CASES = [
+    ("causal-ring4-r3", dict(kv_len=2048, n_ring=4, ring_rank=3)),
+    ("causal-ring4-r0", dict(kv_len=2048, n_ring=4, ring_rank=0)),
+    ("noncausal-ring3-r1", dict(kv_len=1536, n_ring=3, ring_rank=1, causal=False)),
+    ("ragged-250", dict(kv_len=1000, n_ring=4, ring_rank=2)),
+    ("bias-seg", dict(kv_len=2048, n_ring=4, ring_rank=2, bias_len=300, segments="docs", doc_len=(20, 400))),
+    ("seg-noncausal", dict(kv_len=1536, n_ring=3, ring_rank=2, causal=False, segments="docs", doc_len=(5, 120))),
+    ("d128-batch2", dict(head_dim=128, batch=2, heads=3, kv_len=1024, n_ring=2, ring_rank=1, bias_len=77)),
+    ("heads5-ring8", dict(heads=5, kv_len=2048, n_ring=8, ring_rank=5)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_step_chain_matches_oracle_and_fused(gpu, name, kw):
+    w = W.small(name, **kw)
+    t = P.make(w, gpu)
+    out, lse = ra.blockwise_attn_fwd_finalize(_chain(w, t, _ring_order(w)))
+    fo, fl = P.gpu_forward(w, t)
+    torch.cuda.synchronize()
+    ref_o, ref_l = _oracle(w, t)
+    P.assert_close(f"{name} steps vs oracle", P.np64(out), ref_o, "bf16", strict=False)
+    P.assert_lse(lse.cpu().numpy().astype(np.float64), ref_l, "bf16")
+    # the same tiles in the same order as the fused kernel: only the summation order of l differs
+    P.assert_close(f"{name} steps vs fused", P.np64(out), P.np64(fo), "bf16", strict=False)
+    assert float((lse - fl).abs().max()) < 1e-5
+
+
+def test_future_blocks_leave_the_state_unchanged(gpu):
+    # causal: a K/V block wholly after the query block is masked out; folding it in is a no-op
+    w = W.small("future", kv_len=2048, n_ring=4, ring_rank=1, bias_len=64, segments="docs", doc_len=(30, 300))
+    t = P.make(w, gpu)
+    state = _chain(w, t, [1, 0])
+    snap = tuple(x.clone() for x in state)
+    _chain(w, t, [2, 3], state=state, init=False)
+    torch.cuda.synchronize()
+    for a, b in zip(state, snap):
+        assert torch.equal(a, b)
+
+
+def test_init_ignores_what_the_state_holds(gpu):
+    w = W.small("init", kv_len=1024, n_ring=2, ring_rank=1)
+    t = P.make(w, gpu)
+    B, Lq, H, D = t["q"].shape
+    junk = (torch.full((B, Lq, H, D), float("nan"), device=gpu), torch.full((B, H, Lq), 3e38, device=gpu),
+            torch.full((B, H, Lq), -7.0, device=gpu))
+    a = ra.blockwise_attn_fwd_finalize(_chain(w, t, _ring_order(w), state=junk, init=True))
+    b = ra.blockwise_attn_fwd_finalize(_chain(w, t, _ring_order(w)))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_step_order_changes_only_rounding(gpu):
+    w = W.small("order", kv_len=2048, n_ring=8, ring_rank=4, causal=False, heads=3)
+    t = P.make(w, gpu)
+    a = ra.blockwise_attn_fwd_finalize(_chain(w, t, _ring_order(w)))
+    b = ra.blockwise_attn_fwd_finalize(_chain(w, t, [3, 7, 0, 5, 1, 6, 2, 4]))
+    torch.cuda.synchronize()
+    P.assert_close("order", P.np64(b[0]), P.np64(a[0]), "bf16")
+    assert float((a[1] - b[1]).abs().max()) < 1e-4
+
+
+@pytest.mark.parametrize("name,kw,split", [
+    ("causal-r3", dict(kv_len=2048, n_ring=4, ring_rank=3), 2),
+    ("seg-r2", dict(kv_len=2048, n_ring=4, ring_rank=2, segments="docs", doc_len=(10, 200), bias_len=50), 1),
+    ("noncausal-d128", dict(head_dim=128, kv_len=1536, n_ring=3, ring_rank=0, causal=False, heads=3), 1),
+])
+def test_merge_of_partial_results(gpu, name, kw, split):
+    # two devices each fold in a disjoint set of K/V blocks; merging their normalised partial
+    # results (out, lse) must give attention over the union
+    w = W.small(name, **kw)
+    t = P.make(w, gpu)
+    order = _ring_order(w)
+    oa, la = ra.blockwise_attn_fwd_finalize(_chain(w, t, order[:split]))
+    ob, lb = ra.blockwise_attn_fwd_finalize(_chain(w, t, order[split:]))
+    ra.attn_merge(oa, la, ob, lb)
+    torch.cuda.synchronize()
+    ref_o, ref_l = _oracle(w, t)
+    P.assert_close(f"{name} merged", P.np64(oa), ref_o, "bf16", strict=False)
+    P.assert_lse(la.cpu().numpy().astype(np.float64), ref_l, "bf16")
+
+
+def test_merge_with_empty_sides(gpu):
+    # rows whose partial result saw no visible key carry lse = -inf and out = 0: merging such a
+    # side changes nothing, and two empty sides stay empty
+    w = W.small("empty", kv_len=1024, n_ring=2, ring_rank=0)
+    t = P.make(w, gpu)
+    o, l_ = ra.blockwise_attn_fwd_finalize(_chain(w, t, [0]))
+    eo, el = ra.blockwise_attn_fwd_finalize(_chain(w, t, [1]))   # causal: block 1 is all future
+    torch.cuda.synchronize()
+    assert torch.all(torch.isneginf(el)) and torch.all(eo == 0)
+    mo, ml = o.clone(), l_.clone()
+    ra.attn_merge(mo, ml, eo, el)
+    assert torch.equal(mo, o) and torch.equal(ml, l_)
+    eo2, el2 = eo.clone(), el.clone()
+    ra.attn_merge(eo2, el2, eo, el)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isneginf(el2)) and torch.all(eo2 == 0)
+
+
+def test_step_errors(gpu):
+    w = W.small("err", kv_len=1024, n_ring=2, ring_rank=1)
+    t = P.make(w, gpu)
+    k = _block(t["k"], 0, w.block_len)
+    with pytest.raises(ra.RAError, match="equal query and key blocks"):
+        ra.blockwise_attn_fwd_step(t["q"], k[:, :100].contiguous(), k[:, :100].contiguous(), q_pos0=512,
+                                   kv_pos0=0, causal=True)
+    seg = torch.zeros(1, 600, dtype=torch.int32, device=gpu)
+    with pytest.raises(ra.RAError, match="do not cover"):
+        ra.blockwise_attn_fwd_step(t["q"], k, k, None, seg, q_pos0=512, kv_pos0=0, causal=True)
+    qf = t["q"].float()
+    with pytest.raises(ra.RAError, match="RA_BF16"):
+        ra.blockwise_attn_fwd_step(qf, qf, qf, q_pos0=0, kv_pos0=0, causal=True)
