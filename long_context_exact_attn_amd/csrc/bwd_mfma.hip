@@ -121,11 +121,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   float breg = 0.f;
   int sreg = 0;
   bool kok = false;
-  auto load_small = [&](int64_t key0, int64_t kend) {
+  auto load_small = [&](int key0, int kend) {
     if (tid < BK) {
       kok = key0 + tid < kend;
-      const int64_t key = kok ? key0 + tid : key0;
-      if constexpr (HAS_BIAS) breg = p.bias[static_cast<int64_t>(h) * p.bias_len + key % p.bias_len];
+      const int key = kok ? key0 + tid : key0;
+      if constexpr (HAS_BIAS) breg = p.bias[static_cast<int64_t>(h) * p.bias_len + static_cast<unsigned>(key) % static_cast<unsigned>(p.bias_len)];
       if constexpr (HAS_SEG) sreg = p.seg[static_cast<int64_t>(b) * p.Lk + key];
     }
   };
@@ -135,11 +135,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       if constexpr (HAS_SEG) sSeg[slot][tid] = kok ? sreg : 0;
     }
   };
-  auto issue_kv = [&](int64_t key0, int64_t kend, int slot) {
-    const __bf16* kb = kp + kv_bh + key0 * kstride;
-    const __bf16* vb = vp + kv_bh + key0 * kstride;
+  auto issue_kv = [&](int key0, int kend, int slot) {
+    const __bf16* kb = kp + kv_bh + static_cast<int64_t>(key0) * kstride;
+    const __bf16* vb = vp + kv_bh + static_cast<int64_t>(key0) * kstride;
     const bool full = key0 + BK <= kend;
-    const int nvalid = static_cast<int>(kend - key0);
+    const int nvalid = kend - key0;
 #pragma unroll
     for (int jj = 0; jj < NSEG; ++jj) {
       const int off = (full || grow_[jj] < nvalid) ? goff[jj] : goff0[jj];
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 
   RingWalk walk;
   walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
-  int64_t tk0[NS], tke[NS];
+  int tk0[NS], tke[NS];
   bool tok[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -168,9 +168,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   RA_WAIT_VMCNT(0);
   __syncthreads();
 
+  // 32-bit copies of the wave's first query position and last existing row (token positions
+  // are below 2^30, checked on the host), so that per-tile tests stay on the scalar unit
+  const int wpos = static_cast<int>(wpos0);
+  const int wlast = static_cast<int>(wvalid < QW ? wvalid : QW) - 1;
   int slot = 0;
   while (tok[0]) {
-    const int64_t key0 = tk0[0], kend = tke[0];
+    const int key0 = tk0[0], kend = tke[0];
     const int ahead = slot + NS - 1 >= NS ? slot - 1 : slot + NS - 1;   // (slot + NS - 1) % NS
     const bool issue = tok[NS - 1];
     if (issue) {
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 
     const __bf16* Kt = sK[buf];
     const __bf16* Vt = sV[buf];
-    const bool wave_active = wvalid > 0 && !(CAUSAL && key0 > wpos0 + (wvalid < QW ? wvalid : QW) - 1);
+    const bool wave_active = wlast >= 0 && !(CAUSAL && key0 > wpos + wlast);
     if (wave_active) {
       f32x16 S[2][NQB], G[2][NQB];
 #pragma unroll
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       }
       __builtin_amdgcn_s_setprio(0);
 
-      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > wpos0);
+      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > wpos);
       int kseg[2][16];
       if constexpr (HAS_SEG) {
 #pragma unroll
@@ -229,10 +233,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         // key kr of the tile is visible to this lane's query iff kr <= klim and (segments) ids match
         int klim = BK - 1;
         if (need_mask) {
-          klim = static_cast<int>((kend - key0) < BK ? (kend - key0) : BK) - 1;
+          klim = (kend - key0 < BK ? kend - key0 : BK) - 1;
           if constexpr (CAUSAL) {
-            const int64_t rel = wpos0 + nb * 32 + l32 - key0;
-            klim = rel < klim ? static_cast<int>(rel < -1 ? -1 : rel) : klim;
+            const int rel = wpos - key0 + nb * 32 + l32;   // the query's position relative to key 0
+            klim = rel < klim ? (rel < -1 ? -1 : rel) : klim;
           }
         }
         // masked scores become -inf (then P = 0) in a pass of their own, so that tiles
@@ -425,11 +429,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   float lreg = 0.f, dreg = 0.f;
   int sreg = 0;
   bool lok = false;
-  auto load_small = [&](int64_t row0, int64_t rend, int64_t pbase) {
+  auto load_small = [&](int row0, int rend, int pbase) {
     if (tid < BQ) {
-      const int64_t r = row0 + tid;
+      const int r = row0 + tid;
       lok = r < rend;
-      const int64_t rr = lok ? r : row0;
+      const int rr = lok ? r : row0;
       const int64_t li = (static_cast<int64_t>(b) * p.H + h) * p.Lq + rr;
       lreg = p.lse[li];
       dreg = p.delta[li];
@@ -443,11 +447,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       if constexpr (HAS_SEG) sSg[slot][tid] = lok ? sreg : 0;
     }
   };
-  auto issue_qg = [&](int64_t row0, int64_t rend, int slot) {
-    const __bf16* qb_ = qp + q_bh + row0 * qstride;
-    const __bf16* gb_ = gp + q_bh + row0 * qstride;
+  auto issue_qg = [&](int row0, int rend, int slot) {
+    const __bf16* qb_ = qp + q_bh + static_cast<int64_t>(row0) * qstride;
+    const __bf16* gb_ = gp + q_bh + static_cast<int64_t>(row0) * qstride;
     const bool full = row0 + BQ <= rend;
-    const int nvalid = static_cast<int>(rend - row0);
+    const int nvalid = rend - row0;
 #pragma unroll
     for (int jj = 0; jj < NSEG; ++jj) {
       const int off = (full || grow_[jj] < nvalid) ? goff[jj] : goff0[jj];
@@ -459,7 +463,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   // query walk with NS - 1 tiles of lookahead: entry 0 is computed, entry NS - 1 is issued
   QueryWalk walk;
   walk.begin(p.n_ring, j, p.Lb, CAUSAL, kfirst, p.ring_rank);
-  int64_t tr0[NS], tre[NS], tpb[NS];
+  int tr0[NS], tre[NS], tpb[NS];
   bool tok[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -478,9 +482,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   RA_WAIT_VMCNT(0);
   __syncthreads();
 
+  // 32-bit copies for the per-tile tests (positions are below 2^30, checked on the host)
+  const int wkey = static_cast<int>(wkey0);
+  const bool wk_ok = wk0 < p.Lb;
   int slot = 0;
   while (tok[0]) {
-    const int64_t row0 = tr0[0], rend = tre[0], pbase = tpb[0];
+    const int row0 = tr0[0], rend = tre[0], pbase = tpb[0];
     const int ahead = slot + NS - 1 >= NS ? slot - 1 : slot + NS - 1;   // (slot + NS - 1) % NS
     const bool issue = tok[NS - 1];
     if (issue) {
@@ -490,18 +497,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     const int buf = slot;
     const __bf16* Qt = sQ[buf];
     const __bf16* Gt = sG[buf];
-    const int64_t qpos0 = row0 + pbase;                      // global position of the tile's row 0
-    const int64_t nq = (rend - row0) < BQ ? (rend - row0) : BQ;
-    const bool wave_active = wk0 < p.Lb && !(CAUSAL && qpos0 + nq - 1 < wkey0);
+    const int qpos0 = row0 + pbase;                      // global position of the tile's row 0
+    const int nq = (rend - row0) < BQ ? (rend - row0) : BQ;
+    const bool wave_active = wk_ok && !(CAUSAL && qpos0 + nq - 1 < wkey);
     if (wave_active) {
       // rows past the rank's end carry -inf in sL, so their P is 0 and only the causal and
       // segment masks need the selects
-      const bool need_mask = HAS_SEG || (CAUSAL && wkey0 + KW - 1 > qpos0);
+      const bool need_mask = HAS_SEG || (CAUSAL && wkey + KW - 1 > qpos0);
       int krel[NKB];   // the lane's key relative to the tile's row 0, clamped to [0, BQ]
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const int64_t rel = wkey0 + kb * 32 + l32 - qpos0;
-        krel[kb] = rel < 0 ? 0 : (rel > BQ ? BQ : static_cast<int>(rel));
+        const int rel = wkey + kb * 32 + l32 - qpos0;
+        krel[kb] = rel < 0 ? 0 : (rel > BQ ? BQ : rel);
       }
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb) {

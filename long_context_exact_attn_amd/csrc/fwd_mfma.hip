@@ -176,11 +176,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   float breg = 0.f;
   int sreg = 0;
   bool kok = false;
-  auto load_small = [&](int64_t key0, int64_t kend) {
+  auto load_small = [&](int key0, int kend) {
     if (tid < BK) {
       kok = key0 + tid < kend;
-      const int64_t key = kok ? key0 + tid : key0;
-      if constexpr (HAS_BIAS) breg = p.bias[static_cast<int64_t>(h) * p.bias_len + (p.kv_pos0 + key) % p.bias_len];
+      const int key = kok ? key0 + tid : key0;
+      if constexpr (HAS_BIAS)
+        breg = p.bias[static_cast<int64_t>(h) * p.bias_len +
+                      static_cast<unsigned>(static_cast<int>(p.kv_pos0) + key) % static_cast<unsigned>(p.bias_len)];
       if constexpr (HAS_SEG) sreg = p.seg[static_cast<int64_t>(b) * p.seg_len + p.kv_pos0 + key];
     }
   };
@@ -200,11 +202,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       }
     }
   };
-  auto issue_kv = [&](int64_t key0, int64_t kend, int slot) {
-    const __bf16* kb = kp + kv_bh + key0 * kstride;
-    const __bf16* vb = vp + kv_bh + key0 * kstride;
+  auto issue_kv = [&](int key0, int kend, int slot) {
+    const __bf16* kb = kp + kv_bh + static_cast<int64_t>(key0) * kstride;
+    const __bf16* vb = vp + kv_bh + static_cast<int64_t>(key0) * kstride;
     const bool full = key0 + BK <= kend;
-    const int nvalid = static_cast<int>(kend - key0);
+    const int nvalid = kend - key0;
 #pragma unroll
     for (int j = 0; j < NSEG; ++j) {
       const int off = (full || grow_[j] < nvalid) ? goff[j] : goff0[j];
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   // ring walk with NS - 1 tiles of lookahead: T[0] is being computed, T[NS-1] is issued
   RingWalk walk;
   walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
-  int64_t tk0[NS], tke[NS];
+  int tk0[NS], tke[NS];
   bool tok[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -235,9 +237,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   RA_WAIT_VMCNT(0);
   __syncthreads();
 
+  // the wave's first query position and last existing row as 32-bit values (token positions
+  // are below 2^30, checked on the host), so that per-tile tests stay on the scalar unit
+  const int wpos = static_cast<int>(wpos0);
+  const int wlast = static_cast<int>(wvalid < QW ? wvalid : QW) - 1;
   int slot = 0;
   while (tok[0]) {
-    const int64_t key0 = tk0[0], kend = tke[0];
+    const int key0 = tk0[0], kend = tke[0];
     const int ahead = slot + NS - 1 >= NS ? slot - 1 : slot + NS - 1;   // (slot + NS - 1) % NS
     const bool issue = tok[NS - 1];
     if (issue) {
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     const int buf = slot;
     const __bf16* Kt = sK[buf];
     const __bf16* Vt = sV[buf];
-    bool wave_active = wvalid > 0 && !(CAUSAL && key0 > wpos0 + (wvalid < QW ? wvalid : QW) - 1);
+    bool wave_active = wlast >= 0 && !(CAUSAL && key0 > wpos + wlast);
     if constexpr (HAS_SEG) {
       // no key of the tile shares a segment with the wave's queries: every pair is masked
       const int klo = __builtin_amdgcn_readfirstlane(sSegRange[buf][0]);
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         }
       }
 
-      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > wpos0);
+      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > wpos);
       int kseg[2][16];
       if constexpr (HAS_SEG) {
 #pragma unroll
@@ -289,7 +295,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       bf16x8 P[NQB][2][2];   // [query block][key block][16-key step]
 #pragma unroll
       for (int nb = 0; nb < NQB; ++nb) {
-        const int64_t qpos = wpos0 + nb * 32 + l32;
         // logits in log2 units when there is a bias (else raw scores, scaled inside the exp)
         if constexpr (HAS_BIAS) {
 #pragma unroll
@@ -303,10 +308,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         if (need_mask) {
           // key kr of the tile is visible iff kr <= klim (causal and ragged end) and, with
           // segments, its id equals the query's; applied with selects, no branches
-          int klim = static_cast<int>((kend - key0) < BK ? (kend - key0) : BK) - 1;
+          int klim = (kend - key0 < BK ? kend - key0 : BK) - 1;
           if constexpr (CAUSAL) {
-            const int64_t rel = qpos - key0;
-            klim = rel < klim ? static_cast<int>(rel < -1 ? -1 : rel) : klim;
+            const int rel = wpos - key0 + nb * 32 + l32;   // the query's position relative to key 0
+            klim = rel < klim ? (rel < -1 ? -1 : rel) : klim;
           }
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)

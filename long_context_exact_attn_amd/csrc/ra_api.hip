@@ -12,6 +12,8 @@ namespace {
 
 thread_local std::string g_last_error;
 
+constexpr int64_t kMaxPos = int64_t(1) << 30;   // token positions are 32-bit in the kernels
+
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -71,6 +73,10 @@ int check_shape(const ra_shape* s, int32_t n_ring, Checked* c) {
   if (std::isnan(s->scale)) return fail(RA_ERR_ARG, "scale is NaN");
   const int64_t HB = static_cast<int64_t>(s->batch) * s->heads;
   if (HB > (int64_t(1) << 30)) return fail(RA_ERR_SHAPE, "batch*heads too large");
+  // token positions are 32-bit inside the kernels
+  if (s->kv_len >= kMaxPos || s->q_len >= kMaxPos)
+    return fail(RA_ERR_SHAPE, "sequence lengths must be below 2^30 (q_len %lld, kv_len %lld)", (long long)s->q_len,
+                (long long)s->kv_len);
   // the kernels address the rows of one 64-key tile with 32-bit offsets
   if (static_cast<int64_t>(s->heads) * s->head_dim * 64 >= (int64_t(1) << 31))
     return fail(RA_ERR_SHAPE, "heads*head_dim too large (%lld)", (long long)s->heads * s->head_dim);
@@ -106,7 +112,8 @@ int check_mask_args(const ra_shape* s, const float* bias, int64_t q_chunk, int64
   if (Lb > 0 && (Lb % q_chunk != 0 || Lb % k_chunk != 0))
     return fail(RA_ERR_ARG, "q_chunk %lld and k_chunk %lld must divide the ring block length %lld",
                 (long long)q_chunk, (long long)k_chunk, (long long)Lb);
-  if (bias && s->bias_len < 1) return fail(RA_ERR_ARG, "bias given with bias_len %lld", (long long)s->bias_len);
+  if (bias && (s->bias_len < 1 || s->bias_len >= kMaxPos))
+    return fail(RA_ERR_ARG, "bias given with bias_len %lld (must be in [1, 2^30))", (long long)s->bias_len);
   c->p.causal = causal;
   if (!bias) c->p.bias_len = 1;
   return RA_OK;
@@ -297,6 +304,8 @@ int ra_blockwise_attn_fwd_step(const void* q, const void* k, const void* v, cons
     return fail(RA_ERR_SHAPE, "a ring step needs equal query and key blocks (q_len %lld, kv_len %lld)",
                 (long long)shape->q_len, (long long)shape->kv_len);
   if (q_pos0 < 0 || kv_pos0 < 0) return fail(RA_ERR_ARG, "q_pos0 and kv_pos0 must be >= 0");
+  if (q_pos0 + shape->q_len >= kMaxPos || kv_pos0 + shape->kv_len >= kMaxPos)
+    return fail(RA_ERR_SHAPE, "global positions must stay below 2^30");
   if (init != 0 && init != 1) return fail(RA_ERR_ARG, "init must be 0 or 1 (got %d)", init);
   ra_shape blk = *shape;
   blk.ring_rank = 0;   // one block: the walk visits the keys held, causal on the global positions below

@@ -72,12 +72,14 @@ __device__ __forceinline__ int64_t row_offset(int b, int64_t row, int h, int64_t
 // the end of its K/V block (keys at or past kend are padding of a ragged
 // tile and must be treated as invisible).
 struct RingWalk {
+  // key positions fit in 32 bits (the host rejects kv_len >= 2^30), so the walk's compares
+  // stay on the scalar unit
   int n, r, s;
   bool causal;
-  int64_t Lb, plast;  // plast: last global query position of the tile
-  int64_t key0, kend, kstop;
+  int Lb, plast;  // plast: last global query position of the tile
+  int key0, kend, kstop;
   __device__ void begin(int n_, int r_, int64_t Lb_, bool causal_, int64_t plast_) {
-    n = n_; r = r_; Lb = Lb_; causal = causal_; plast = plast_;
+    n = n_; r = r_; Lb = static_cast<int>(Lb_); causal = causal_; plast = static_cast<int>(plast_);
     s = -1; key0 = 0; kend = 0; kstop = 0;
   }
   template <int BK>
@@ -89,7 +91,7 @@ struct RingWalk {
       int j = r - s;
       if (j < 0) j += n;
       if (causal && j > r) continue;   // a block from the future: fully masked, skipped
-      key0 = static_cast<int64_t>(j) * Lb;
+      key0 = j * Lb;
       kend = key0 + Lb;
       kstop = (causal && j == r) ? (plast + 1 < kend ? plast + 1 : kend) : kend;
     }
@@ -103,14 +105,16 @@ struct RingWalk {
 // Under a causal mask ranks before j are skipped and, in rank j itself, query
 // tiles that end before the K/V tile's first key are skipped.
 struct QueryWalk {
+  // 32-bit rows and positions (below 2^30, checked on the host): the compares stay scalar
   int n, j, s, rank_only;
   bool causal;
-  int64_t Lb, kfirst;   // kfirst: first global key of the K/V tile
-  int64_t row0, rend, rstop;   // local query rows [row0, row0+BQ) of q; rend: end of the rank's rows
-  int64_t pos_base;            // global position of local row 0 of the current rank
+  int Lb, kfirst;   // kfirst: first global key of the K/V tile
+  int row0, rend, rstop;   // local query rows [row0, row0+BQ) of q; rend: end of the rank's rows
+  int pos_base;            // global position of local row 0 of the current rank
   int cur_rank;
   __device__ void begin(int n_, int j_, int64_t Lb_, bool causal_, int64_t kfirst_, int rank_only_) {
-    n = n_; j = j_; Lb = Lb_; causal = causal_; kfirst = kfirst_; rank_only = rank_only_;
+    n = n_; j = j_; Lb = static_cast<int>(Lb_); causal = causal_; kfirst = static_cast<int>(kfirst_);
+    rank_only = rank_only_;
     s = -1; row0 = 0; rend = 0; rstop = 0; pos_base = 0; cur_rank = 0;
   }
   template <int BQ>
@@ -124,13 +128,13 @@ struct QueryWalk {
       if (rank_only >= 0 && r != rank_only) continue;
       if (causal && r < j) continue;        // queries before the block see none of it
       cur_rank = r;
-      int64_t local0 = rank_only >= 0 ? 0 : static_cast<int64_t>(r) * Lb;   // first local row of rank r
-      pos_base = static_cast<int64_t>(r) * Lb - local0;                       // global pos = local row + pos_base
+      const int local0 = rank_only >= 0 ? 0 : r * Lb;   // first local row of rank r
+      pos_base = r * Lb - local0;                       // global pos = local row + pos_base
       rend = local0 + Lb;
       row0 = local0;
       if (causal && r == j) {
         // skip whole query tiles that end before kfirst: first row with pos >= kfirst
-        int64_t first_row = kfirst - pos_base;
+        const int first_row = kfirst - pos_base;
         if (first_row > row0) row0 += ((first_row - row0) / BQ) * BQ;
       }
       rstop = rend;

@@ -175,3 +175,17 @@ def test_ring_step_validation():
     assert rc == -1 and b"lse_b" in lib.ra_last_error()
     rc = lib.ra_attn_merge(None, FAKE, FAKE, FAKE, ctypes.byref(S(batch=-2)), None)
     assert rc == -2
+
+
+@needs_cpu
+def test_positions_must_fit_32_bits():
+    lib = _lib()
+    s = api.Shape(1, 2, 64, -1, 1 << 30, 1 << 30, 0, 0.0, api.RA_BF16)
+    assert _fwd(lib, s, n_ring=1, q_chunk=1 << 30, k_chunk=1 << 30) == -2
+    assert b"2^30" in lib.ra_last_error()
+    s = api.Shape(1, 2, 64, -1, 512, 512, 0, 0.0, api.RA_BF16)
+    rc = lib.ra_blockwise_attn_fwd_step(FAKE, FAKE, FAKE, None, None, 0, (1 << 30) - 100, 0, 1, None, FAKE, FAKE, 1,
+                                        ctypes.byref(s), None)
+    assert rc == -2 and b"2^30" in lib.ra_last_error()
+    s = api.Shape(1, 2, 64, -1, 512, 512, 1 << 30, 0.0, api.RA_BF16)
+    assert _fwd(lib, s, n_ring=1, q_chunk=512, k_chunk=512, bias=FAKE) == -1
