@@ -57,6 +57,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   __shared__ float sBias[NS][BK];
   __shared__ __attribute__((aligned(16))) int sSeg[NS][BK];
   __shared__ int sSegRange[NS][2];   // smallest and largest segment id among the tile's keys
+  __shared__ int sWaveSeg[kWaves][2];  // each wave's range of query segment ids
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-derived values stay scalar
@@ -117,6 +118,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     }
     qseg_lo = __builtin_amdgcn_readfirstlane(wave_min_i32(lo));
     qseg_hi = __builtin_amdgcn_readfirstlane(wave_max_i32(hi));
+  }
+  // the workgroup's range of query segment ids: a K/V tile none of whose keys carries an id
+  // in it has no visible pair with any of the workgroup's queries, and is neither loaded
+  // nor computed (exact for any ids)
+  int gseg_lo = 0, gseg_hi = 0;
+  if constexpr (HAS_SEG) {
+    if (lane == 0) {
+      sWaveSeg[wave][0] = qseg_lo;
+      sWaveSeg[wave][1] = qseg_hi;
+    }
+    __syncthreads();
+    gseg_lo = sWaveSeg[0][0];
+    gseg_hi = sWaveSeg[0][1];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      gseg_lo = min(gseg_lo, sWaveSeg[w][0]);
+      gseg_hi = max(gseg_hi, sWaveSeg[w][1]);
+    }
   }
 
   const float c = p.scale * kLog2e;   // raw score -> log2 units
@@ -218,11 +237,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   // ring walk with NS - 1 tiles of lookahead: T[0] is being computed, T[NS-1] is issued
   RingWalk walk;
   walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
+  // With segment ids the walk passes over tiles that share no id with the workgroup's
+  // queries.  Which tiles those are is found 64 tiles at a time: for a window of up to 64
+  // tiles from key swin to swend (never past the end of the block scanned), bit t of smask
+  // says whether some key of tile t has an id in [gseg_lo, gseg_hi] (one coalesced load of
+  // 64 ids and one ballot per tile).
+  uint64_t smask = 0;
+  int swin = 0, swend = 0;
+  auto seg_scan = [&](int win0, int kend) {
+    const int* __restrict__ ids = p.seg + static_cast<int64_t>(b) * p.seg_len + p.kv_pos0;
+    uint64_t m = 0;
+#pragma unroll
+    for (int g = 0; g < 64; g += 16) {
+      int id[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = win0 + (g + i) * BK + lane;
+        id[i] = key < kend ? ids[key] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool in_block = win0 + (g + i) * BK + lane < kend;   // keys past the block never match
+        if (__ballot(in_block && id[i] >= gseg_lo && id[i] <= gseg_hi) != 0) m |= uint64_t(1) << (g + i);
+      }
+    }
+    return m;
+  };
+  auto next_tile = [&]() -> bool {
+    while (walk.next<BK>()) {
+      if constexpr (!HAS_SEG) return true;
+      const int key0 = walk.key0;
+      if (key0 < swin || key0 >= swend) {
+        swin = key0;
+        swend = min(key0 + 64 * BK, walk.kend);
+        smask = seg_scan(swin, walk.kend);
+      }
+      const int bit = (key0 - swin) / BK;
+      const uint64_t rest = smask >> bit;
+      if (rest & 1) return true;
+      // on to the window's next tile with a matching id, or past the window
+      const int skip = rest ? __builtin_ctzll(rest) : 64 - bit;
+      walk.key0 += (skip - 1) * BK;   // next() adds the last BK
+    }
+    return false;
+  };
   int tk0[NS], tke[NS];
   bool tok[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    tok[i] = nrows > 0 && walk.next<BK>();
+    tok[i] = nrows > 0 && next_tile();
     tk0[i] = walk.key0;
     tke[i] = walk.kend;
   }
@@ -393,7 +456,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       tk0[i] = tk0[i + 1];
       tke[i] = tke[i + 1];
     }
-    tok[NS - 1] = walk.next<BK>();
+    tok[NS - 1] = next_tile();
     tk0[NS - 1] = walk.key0;
     tke[NS - 1] = walk.kend;
   }

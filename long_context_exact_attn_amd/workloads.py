@@ -36,7 +36,8 @@ class Workload:
     causal: bool = True
     std: float = 0.5             # q, k, v ~ N(0, 1) * std
     bias_len: int = 0            # 0: no bias; else bias ~ N(0,1) of shape [heads, bias_len]
-    segments: str = "none"       # "none", "zeros" (all ids 0) or "docs" (packed documents)
+    segments: str = "none"       # "none", "zeros" (all ids 0), "docs" (packed documents) or
+                                 # "scattered" (unsorted runs of a few ids, extremes included)
     doc_len: tuple = (512, 16384)
     backward: bool = False       # also draw dout ~ N(0, 1)
     seed: int = 0
@@ -88,6 +89,21 @@ def doc_segment_ids(batch, kv_len, lo, hi, seed):
     return ids
 
 
+def scattered_segment_ids(batch, kv_len, seed, max_run=200):
+    """Unsorted ids: runs of 1..max_run positions, each run's id drawn from a small set that
+    includes the int32 extremes.  int32 [batch, kv_len]."""
+    rng = np.random.default_rng(seed)
+    alphabet = np.array([-2**31, -5, 3, 7, 2**31 - 1], dtype=np.int64)
+    ids = np.empty((batch, kv_len), dtype=np.int32)
+    for b in range(batch):
+        pos = 0
+        while pos < kv_len:
+            n = int(rng.integers(1, max_run, endpoint=True))
+            ids[b, pos:pos + n] = alphabet[rng.integers(len(alphabet))]
+            pos += n
+    return ids
+
+
 def _normal(shape, gen, device, std, dtype):
     x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
     if std != 1.0:
@@ -123,6 +139,8 @@ def make(w: Workload, device="cpu", seed: Optional[int] = None):
         t["segment_ids"] = torch.zeros((B, w.kv_len), dtype=torch.int32, device=dev)
     elif w.segments == "docs":
         t["segment_ids"] = torch.from_numpy(doc_segment_ids(B, w.kv_len, *w.doc_len, seed)).to(dev)
+    elif w.segments == "scattered":
+        t["segment_ids"] = torch.from_numpy(scattered_segment_ids(B, w.kv_len, seed)).to(dev)
     if w.backward:
         t["dout"] = _normal((B, w.q_len, H, D), gen, dev, 1.0, dt)
     return t
@@ -139,4 +157,4 @@ def small(name="small", *, batch=1, heads=2, head_dim=64, kv_len=512, n_ring=2, 
                     backward=backward, seed=seed)
 
 
-__all__ = ["Workload", "WORKLOADS", "make", "small", "doc_segment_ids", "torch_dtype", "replace", "field"]
+__all__ = ["Workload", "WORKLOADS", "make", "small", "doc_segment_ids", "scattered_segment_ids", "torch_dtype", "replace", "field"]

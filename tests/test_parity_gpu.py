@@ -92,6 +92,13 @@ SWEEP = [
     ("batch3-heads5", dict(batch=3, heads=5, kv_len=640, n_ring=5)),
     ("n_ring1", dict(kv_len=1000, n_ring=1)),
     ("f32-causal-seg", dict(dtype="f32", kv_len=600, n_ring=3, segments="docs", doc_len=(10, 150), bias_len=33)),
+    # several 64-tile windows of segment ids per ring block, long and short documents
+    ("docs-long", dict(kv_len=12288, n_ring=3, ring_rank=2, segments="docs", doc_len=(50, 3000), heads=2)),
+    ("docs-long-d128", dict(head_dim=128, kv_len=9216, n_ring=2, segments="docs", doc_len=(20, 5000), heads=2,
+                            bias_len=512)),
+    # unsorted ids, int32 extremes included: tile skipping must stay exact for any ids
+    ("ids-scattered", dict(kv_len=6144, n_ring=3, segments="scattered", heads=2)),
+    ("ids-scattered-noncausal", dict(kv_len=2048, n_ring=2, causal=False, segments="scattered", bias_len=77)),
     ("f32-d128-rank1", dict(dtype="f32", head_dim=128, kv_len=512, n_ring=4, ring_rank=1)),
 ]
 

@@ -36,3 +36,14 @@ def test_named_workloads_shapes():
     assert (w.batch, w.heads, w.head_dim, w.block_len, w.bias_len) == (2, 32, 128, 4096, 4096)
     t = W.make(W.WORKLOADS["tiny-f32-1k"])
     assert t["q"].dtype == torch.float32 and torch.all(t["segment_ids"] == 0)
+
+
+def test_scattered_segments_recipe():
+    ids = W.scattered_segment_ids(2, 5000, seed=3)
+    assert ids.dtype == np.int32 and ids.shape == (2, 5000)
+    assert np.array_equal(ids, W.scattered_segment_ids(2, 5000, seed=3))
+    vals = set(np.unique(ids).tolist())
+    assert vals <= {-2**31, -5, 3, 7, 2**31 - 1} and {-2**31, 2**31 - 1} <= vals
+    # unsorted: ids go down as well as up along the sequence
+    d = np.diff(ids[0].astype(np.int64))
+    assert (d > 0).any() and (d < 0).any()
