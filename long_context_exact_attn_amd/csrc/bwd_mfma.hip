@@ -44,6 +44,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   __shared__ __attribute__((aligned(16))) __bf16 sV[NS][TILE];
   __shared__ float sBias[NS][BK];
   __shared__ __attribute__((aligned(16))) int sSeg[NS][BK];
+  __shared__ int sWaveSeg[kWaves][2];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -95,6 +96,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     lse2[nb] = (ok && L != -INFINITY) ? L * kLog2e : INFINITY;
     dlt[nb] = ok ? p.delta[li] : 0.f;
     qseg[nb] = (HAS_SEG && ok) ? p.seg[static_cast<int64_t>(b) * p.Lk + wpos0 + nb * 32 + l32] : 0;
+  }
+  // the workgroup's range of query segment ids: K/V tiles with no key id in it are passed over
+  int gseg_lo = 0, gseg_hi = 0;
+  if constexpr (HAS_SEG) {
+    int lo = INT32_MAX, hi = INT32_MIN;
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb)
+      if (wrow0 + nb * 32 + l32 < p.Lb) {
+        lo = min(lo, qseg[nb]);
+        hi = max(hi, qseg[nb]);
+      }
+    wg_id_range(lo, hi, sWaveSeg, wave, lane, gseg_lo, gseg_hi);
   }
 
   const float c = p.scale * kLog2e;
@@ -150,11 +163,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 
   RingWalk walk;
   walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
+  SegTileFilter filt;   // with segment ids: pass over tiles sharing no id with the queries
+  const int* __restrict__ kv_ids = HAS_SEG ? p.seg + static_cast<int64_t>(b) * p.Lk : nullptr;
+  auto next_tile = [&]() -> bool {
+    while (walk.next<BK>()) {
+      if constexpr (!HAS_SEG) return true;
+      static_assert(BK == 64, "the segment filter works in 64-key tiles");
+      const int skip = filt.skip(kv_ids, walk.key0, walk.kend, gseg_lo, gseg_hi, lane);
+      if (skip == 0) return true;
+      walk.key0 += (skip - 1) * BK;   // next() adds the last BK
+    }
+    return false;
+  };
   int tk0[NS], tke[NS];
   bool tok[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    tok[i] = nrows > 0 && walk.next<BK>();
+    tok[i] = nrows > 0 && next_tile();
     tk0[i] = walk.key0;
     tke[i] = walk.kend;
   }
@@ -301,7 +326,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       tk0[i] = tk0[i + 1];
       tke[i] = tke[i + 1];
     }
-    tok[NS - 1] = walk.next<BK>();
+    tok[NS - 1] = next_tile();
     tk0[NS - 1] = walk.key0;
     tke[NS - 1] = walk.kend;
   }
@@ -351,6 +376,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   __shared__ __attribute__((aligned(16))) float sL[NS][BQ];    // -lse * log2e (-inf: row contributes nothing)
   __shared__ __attribute__((aligned(16))) float sDl[NS][BQ];   // Delta
   __shared__ __attribute__((aligned(16))) int sSg[NS][BQ];     // segment id of the query
+  __shared__ int sWaveSeg[kWaves][2];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -396,6 +422,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     }
     kbias[kb] = (HAS_BIAS && ok) ? p.bias[static_cast<int64_t>(h) * p.bias_len + key % p.bias_len] * kLog2e : 0.f;
     ksg[kb] = (HAS_SEG && ok) ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
+  }
+  // the workgroup's range of key segment ids: query tiles with no id in it are passed over
+  int gseg_lo = 0, gseg_hi = 0;
+  if constexpr (HAS_SEG) {
+    int lo = INT32_MAX, hi = INT32_MIN;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      if (wk0 + kb * 32 + l32 < p.Lb) {
+        lo = min(lo, ksg[kb]);
+        hi = max(hi, ksg[kb]);
+      }
+    wg_id_range(lo, hi, sWaveSeg, wave, lane, gseg_lo, gseg_hi);
   }
 
   const float c = p.scale * kLog2e;
@@ -463,11 +501,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   // query walk with NS - 1 tiles of lookahead: entry 0 is computed, entry NS - 1 is issued
   QueryWalk walk;
   walk.begin(p.n_ring, j, p.Lb, CAUSAL, kfirst, p.ring_rank);
+  SegTileFilter filt;   // with segment ids: pass over query tiles sharing no id with the keys
+  const int* __restrict__ q_ids = HAS_SEG ? p.seg + static_cast<int64_t>(b) * p.Lk : nullptr;
+  auto next_tile = [&]() -> bool {
+    while (walk.next<BQ>()) {
+      if constexpr (!HAS_SEG) return true;
+      static_assert(BQ == 64, "the segment filter works in 64-query tiles");
+      // local rows of the current rank: the id of row q sits at position pos_base + q
+      const int skip = filt.skip(q_ids + walk.pos_base, walk.row0, walk.rend, gseg_lo, gseg_hi, lane);
+      if (skip == 0) return true;
+      walk.row0 += (skip - 1) * BQ;   // next() adds the last BQ
+    }
+    return false;
+  };
   int tr0[NS], tre[NS], tpb[NS];
   bool tok[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    tok[i] = walk.next<BQ>();
+    tok[i] = next_tile();
     tr0[i] = walk.row0;
     tre[i] = walk.rend;
     tpb[i] = walk.pos_base;
@@ -616,7 +667,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       tre[i] = tre[i + 1];
       tpb[i] = tpb[i + 1];
     }
-    tok[NS - 1] = walk.next<BQ>();
+    tok[NS - 1] = next_tile();
     tr0[NS - 1] = walk.row0;
     tre[NS - 1] = walk.rend;
     tpb[NS - 1] = walk.pos_base;

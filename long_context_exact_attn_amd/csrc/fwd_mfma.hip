@@ -123,20 +123,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   // in it has no visible pair with any of the workgroup's queries, and is neither loaded
   // nor computed (exact for any ids)
   int gseg_lo = 0, gseg_hi = 0;
-  if constexpr (HAS_SEG) {
-    if (lane == 0) {
-      sWaveSeg[wave][0] = qseg_lo;
-      sWaveSeg[wave][1] = qseg_hi;
-    }
-    __syncthreads();
-    gseg_lo = sWaveSeg[0][0];
-    gseg_hi = sWaveSeg[0][1];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      gseg_lo = min(gseg_lo, sWaveSeg[w][0]);
-      gseg_hi = max(gseg_hi, sWaveSeg[w][1]);
-    }
-  }
+  if constexpr (HAS_SEG) wg_id_range(qseg_lo, qseg_hi, sWaveSeg, wave, lane, gseg_lo, gseg_hi);
 
   const float c = p.scale * kLog2e;   // raw score -> log2 units
   float m[NQB], lsum[NQB];
@@ -238,45 +225,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   RingWalk walk;
   walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
   // With segment ids the walk passes over tiles that share no id with the workgroup's
-  // queries.  Which tiles those are is found 64 tiles at a time: for a window of up to 64
-  // tiles from key swin to swend (never past the end of the block scanned), bit t of smask
-  // says whether some key of tile t has an id in [gseg_lo, gseg_hi] (one coalesced load of
-  // 64 ids and one ballot per tile).
-  uint64_t smask = 0;
-  int swin = 0, swend = 0;
-  auto seg_scan = [&](int win0, int kend) {
-    const int* __restrict__ ids = p.seg + static_cast<int64_t>(b) * p.seg_len + p.kv_pos0;
-    uint64_t m = 0;
-#pragma unroll
-    for (int g = 0; g < 64; g += 16) {
-      int id[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = win0 + (g + i) * BK + lane;
-        id[i] = key < kend ? ids[key] : 0;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bool in_block = win0 + (g + i) * BK + lane < kend;   // keys past the block never match
-        if (__ballot(in_block && id[i] >= gseg_lo && id[i] <= gseg_hi) != 0) m |= uint64_t(1) << (g + i);
-      }
-    }
-    return m;
-  };
+  // queries (windows of 64 tiles, see SegTileFilter).
+  SegTileFilter filt;
+  const int* __restrict__ kv_ids = HAS_SEG ? p.seg + static_cast<int64_t>(b) * p.seg_len + p.kv_pos0 : nullptr;
   auto next_tile = [&]() -> bool {
     while (walk.next<BK>()) {
       if constexpr (!HAS_SEG) return true;
-      const int key0 = walk.key0;
-      if (key0 < swin || key0 >= swend) {
-        swin = key0;
-        swend = min(key0 + 64 * BK, walk.kend);
-        smask = seg_scan(swin, walk.kend);
-      }
-      const int bit = (key0 - swin) / BK;
-      const uint64_t rest = smask >> bit;
-      if (rest & 1) return true;
-      // on to the window's next tile with a matching id, or past the window
-      const int skip = rest ? __builtin_ctzll(rest) : 64 - bit;
+      static_assert(BK == 64, "the segment filter works in 64-key tiles");
+      const int skip = filt.skip(kv_ids, walk.key0, walk.kend, gseg_lo, gseg_hi, lane);
+      if (skip == 0) return true;
       walk.key0 += (skip - 1) * BK;   // next() adds the last BK
     }
     return false;

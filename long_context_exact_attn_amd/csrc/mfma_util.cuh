@@ -132,6 +132,72 @@ __device__ __forceinline__ int wave_max_i32(int x) {
   return x;
 }
 
+// Smallest and largest id over the workgroup (each lane passes the range of its own ids,
+// INT32_MAX / INT32_MIN for none); every wave gets the same result.  Contains a barrier.
+template <int NW>
+__device__ __forceinline__ void wg_id_range(int lo, int hi, int (&s)[NW][2], int wave, int lane, int& glo, int& ghi) {
+  lo = wave_min_i32(lo);
+  hi = wave_max_i32(hi);
+  if (lane == 0) {
+    s[wave][0] = lo;
+    s[wave][1] = hi;
+  }
+  __syncthreads();
+  glo = s[0][0];
+  ghi = s[0][1];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    glo = min(glo, s[w][0]);
+    ghi = max(ghi, s[w][1]);
+  }
+}
+
+// Tile filter for segment ids: bit t of the result is set iff some position q in
+// [start + 64 t, start + 64 t + 64) with q < end has lo <= ids[q] <= hi.  Each of the 64
+// tiles costs one coalesced load of 64 ids and one ballot; the result is wave-uniform.
+__device__ __forceinline__ uint64_t seg_window_mask(const int* __restrict__ ids, int start, int end, int lo, int hi,
+                                                    int lane) {
+  uint64_t m = 0;
+#pragma unroll
+  for (int g = 0; g < 64; g += 16) {
+    int id[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = start + (g + i) * 64 + lane;
+      id[i] = q < end ? ids[q] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool inside = start + (g + i) * 64 + lane < end;
+      if (__ballot(inside && id[i] >= lo && id[i] <= hi) != 0) m |= uint64_t(1) << (g + i);
+    }
+  }
+  return m;
+}
+
+// Lookahead filter over a tile walk (tiles of 64 positions): passes over the tiles whose
+// bit is clear.  The window [win, wend) of at most 64 tiles never extends past the end of
+// the block or rank it was scanned in, so a window scanned for one block is never used
+// for another.
+struct SegTileFilter {
+  uint64_t mask = 0;
+  int win = 0, wend = 0;
+  // pos: first position of the walk's current tile; end: end of its block; ids: id of
+  // position q at ids[q].  Returns 0 if the tile is to be visited, else how many tiles to
+  // advance (past the window when none of its remaining tiles matches).
+  __device__ __forceinline__ int skip(const int* __restrict__ ids, int pos, int end, int lo, int hi, int lane) {
+    if (pos < win || pos >= wend) {
+      win = pos;
+      wend = min(pos + 64 * 64, end);
+      mask = seg_window_mask(ids, pos, end, lo, hi, lane);
+    }
+    const int bit = (pos - win) >> 6;
+    const uint64_t rest = mask >> bit;
+    if (rest & 1) return 0;
+    return rest ? __builtin_ctzll(rest) : 64 - bit;
+  }
+};
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
