@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="share-1m-r7")
+    ap.add_argument("--ring-rank", type=int, default=None,
+                    help="for a one-rank workload: time ring rank r instead (a sweep line, not the bench line)")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward alone (not the bench line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -129,6 +131,11 @@ def main():
     from long_context_exact_attn_amd import workloads as W
 
     w = W.WORKLOADS[args.workload]
+    if args.ring_rank is not None:
+        if w.ring_rank < 0 or not 0 <= args.ring_rank < w.n_ring:
+            print(f"--ring-rank needs a one-rank workload and a rank in [0, {w.n_ring})", file=sys.stderr)
+            sys.exit(2)
+        w = W.replace(w, ring_rank=args.ring_rank, name=f"{w.name.rsplit('-r', 1)[0]}-r{args.ring_rank}")
     if not w.backward and not args.fwd_only:
         w = W.replace(w, backward=True)
     dev = torch.device("cuda:0")
