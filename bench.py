@@ -69,6 +69,10 @@ def parse():
     ap.add_argument("--ring-rank", type=int, default=None,
                     help="for a one-rank workload: time ring rank r instead (a sweep line, not the bench line)")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward alone (not the bench line)")
+    ap.add_argument("--ring-steps", action="store_true",
+                    help="with --fwd-only and a one-rank workload: run the forward as one ra_blockwise_attn_fwd_step "
+                         "per visible ring step plus ra_blockwise_attn_fwd_finalize (the per-step path a "
+                         "multi-GPU ring calls), K/V blocks already in contiguous receive buffers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash and exit")
@@ -136,6 +140,9 @@ def main():
             print(f"--ring-rank needs a one-rank workload and a rank in [0, {w.n_ring})", file=sys.stderr)
             sys.exit(2)
         w = W.replace(w, ring_rank=args.ring_rank, name=f"{w.name.rsplit('-r', 1)[0]}-r{args.ring_rank}")
+    if args.ring_steps and not (args.fwd_only and w.ring_rank >= 0 and w.dtype == "bf16"):
+        print("--ring-steps needs --fwd-only and a one-rank bf16 workload", file=sys.stderr)
+        sys.exit(2)
     if not w.backward and not args.fwd_only:
         w = W.replace(w, backward=True)
     dev = torch.device("cuda:0")
@@ -150,12 +157,33 @@ def main():
         delta = torch.empty_like(lse)
     names = ["fwd"] if args.fwd_only else ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
 
+    if args.ring_steps:
+        # the blocks a device meets, in ring order, as contiguous receive buffers; causal blocks from
+        # the future are not sent
+        Lb, r, n = w.block_len, w.ring_rank, w.n_ring
+        order = [(r - s_) % n for s_ in range(n)]
+        order = [j for j in order if not (w.causal and j > r)]
+        blocks = [(j, k[:, j * Lb:(j + 1) * Lb].contiguous(), v[:, j * Lb:(j + 1) * Lb].contiguous()) for j in order]
+        B_, Lq_, H_, D_ = q.shape
+        state = (torch.empty((B_, Lq_, H_, D_), dtype=torch.float32, device=dev),
+                 torch.empty((B_, H_, Lq_), dtype=torch.float32, device=dev),
+                 torch.empty((B_, H_, Lq_), dtype=torch.float32, device=dev))
+
+    def forward():
+        if not args.ring_steps:
+            ra.blockwise_attn_fwd(q, k, v, bias, seg, out=out, lse=lse, **kw)
+            return
+        for i_, (j, kb, vb) in enumerate(blocks):
+            ra.blockwise_attn_fwd_step(q, kb, vb, bias, seg, q_pos0=r * Lb, kv_pos0=j * Lb, causal=w.causal,
+                                       state=state, init=i_ == 0)
+        ra.blockwise_attn_fwd_finalize(state, out=out, lse=lse)
+
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record()
         mark(0)
-        ra.blockwise_attn_fwd(q, k, v, bias, seg, out=out, lse=lse, **kw)
+        forward()
         mark(1)
         if args.fwd_only:
             return
@@ -224,7 +252,7 @@ def main():
         "config": {"workload": f"{w.name}: one device's share of a {w.kv_len}-token causal context "
                                f"(ring rank {w.ring_rank} of {w.n_ring}), {w.q_len} local queries, "
                                f"{w.heads} heads, head_dim {w.head_dim}" if w.ring_rank >= 0 else w.name,
-                   "pass": "fwd" if args.fwd_only else "fwd+bwd",
+                   "pass": ("fwd (ring steps)" if args.ring_steps else "fwd") if args.fwd_only else "fwd+bwd",
                    "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim, "q_len": w.q_len,
                    "kv_len": w.kv_len, "n_ring": w.n_ring, "ring_rank": w.ring_rank, "causal": w.causal,
                    "q_chunk": w.q_chunk, "k_chunk": w.k_chunk, "bias": w.bias_len > 0,
