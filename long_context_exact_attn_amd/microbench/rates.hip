@@ -68,6 +68,36 @@ __global__ __launch_bounds__(256) void k_mix(float* out, float seed) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// wave-specialised: in a 512-thread workgroup (two waves per SIMD) waves 0-3 run only matrix
+// products and waves 4-7 only VALU work (OP 0: v_exp_f32, 1: v_fma_f32; 8 independent chains);
+// timing each part alone and both together shows whether the SIMD overlaps them across waves.
+template <int OP>
+__global__ __launch_bounds__(512) void k_split(float* out, float seed, int n_mfma, int n_valu) {
+  const int w = threadIdx.x >> 6;
+  float s = 0;
+  if (w < 4) {
+    bf16x8 a, b;
+    for (int i = 0; i < 8; ++i) { a[i] = (__bf16)(seed * i); b[i] = (__bf16)(seed + i); }
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < n_mfma; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+    for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  } else {
+    float x[8];
+    for (int i = 0; i < 8; ++i) x[i] = seed * (threadIdx.x + i);
+    for (int it = 0; it < n_valu; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = OP == 0 ? __builtin_amdgcn_exp2f(-x[i]) : __builtin_fmaf(x[i], 0.999f, 0.001f);
+    }
+    for (int i = 0; i < 8; ++i) s += x[i];
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 #define CHECK(x)                                                                  \
   do {                                                                            \
     hipError_t e_ = (x);                                                          \
@@ -128,6 +158,20 @@ int main() {
     float m32 = timeit([&] { hipLaunchKernelGGL(k_mix<32>, dim3(g), dim3(256), 0, 0, out, 0.5f); });
     float m64 = timeit([&] { hipLaunchKernelGGL(k_mix<64>, dim3(g), dim3(256), 0, 0, out, 0.5f); });
     printf("mix wg/CU=%d (4 mfma + E exp per iter): E=0 %.3f ms, E=16 %.3f, E=32 %.3f, E=64 %.3f\n", wpc, m0, m16, m32, m64);
+  }
+  for (int op = 0; op < 2; ++op) {
+    const int g = cus;   // one 8-wave workgroup per CU
+    auto run = [&](int nm, int nv) {
+      return timeit([&] {
+        if (op == 0) hipLaunchKernelGGL(k_split<0>, dim3(g), dim3(512), 0, 0, out, 0.5f, nm, nv);
+        else hipLaunchKernelGGL(k_split<1>, dim3(g), dim3(512), 0, 0, out, 0.5f, nm, nv);
+      });
+    };
+    for (int nv : {N, 2 * N}) {
+      const float tm = run(N, 0), tv = run(0, nv), tb = run(N, nv);
+      printf("split %s: mfma wave %d x 4 MFMA %.3f ms; valu wave %d x 8 %s %.3f ms; both %.3f ms (sum %.3f, max %.3f)\n",
+             op == 0 ? "exp" : "fma", N, tm, nv, op == 0 ? "exp" : "fma", tv, tb, tm + tv, tm > tv ? tm : tv);
+    }
   }
   CHECK(hipFree(out));
   return 0;
