@@ -47,6 +47,29 @@ def test_share_1m_rank7_sampled_rows(gpu):
     _check_forward(w, gpu, rows=P.sample_rows(w, 96, seed=2), heads=slice(0, 16, 5))
 
 
+def test_share_1m_rank7_backward_sampled(gpu):
+    # the full backward at the 1M-token share, in the launch configuration bench.py times:
+    # dQ on sampled rows of two heads against the oracle (which forms lse and Delta itself),
+    # dK / dV through properties that hold at any size
+    w = W.replace(W.WORKLOADS["share-1m-r7"], backward=True)
+    t = P.make(w, gpu)
+    out, lse = P.gpu_forward(w, t)
+    dq, dk, dv = P.gpu_backward(w, t, out, lse)
+    torch.cuda.synchronize()
+    rows = P.sample_rows(w, 32, seed=4)
+    import oracle
+    for h in (0, 11):
+        d = P.oracle_inputs(t, heads=slice(h, h + 1), rows=rows)
+        rdq, _, _, _ = oracle.backward(d["q"], d["k"], d["v"], d["dout"], q_pos=w.q_positions()[rows], causal=True)
+        P.assert_close(f"{w.name} dq[h={h}]", P.np64(dq[:, rows, h:h + 1]), rdq, "bf16")
+    # sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i on every head (the keys see only this rank's queries)
+    sdk = dk.float().sum(dim=1)
+    sdv, sdo = dv.float().sum(dim=1), t["dout"].float().sum(dim=1)
+    scale_k = dk.float().abs().sum(dim=1)
+    assert torch.all(sdk.abs() <= 2e-2 * scale_k + 1e-3), float((sdk.abs() / scale_k).max())
+    assert torch.allclose(sdv, sdo, rtol=2e-2, atol=2e-1), float((sdv - sdo).abs().max())
+
+
 def test_packed_docs_64k_sampled_rows(gpu):
     w = W.WORKLOADS["packed-docs-64k"]
     _check_forward(w, gpu, rows=P.sample_rows(w, 192, seed=3), heads=slice(0, 32, 7))
