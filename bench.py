@@ -70,9 +70,9 @@ def parse():
                     help="for a one-rank workload: time ring rank r instead (a sweep line, not the bench line)")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward alone (not the bench line)")
     ap.add_argument("--ring-steps", action="store_true",
-                    help="with --fwd-only and a one-rank workload: run the forward as one ra_blockwise_attn_fwd_step "
-                         "per visible ring step plus ra_blockwise_attn_fwd_finalize (the per-step path a "
-                         "multi-GPU ring calls), K/V blocks already in contiguous receive buffers")
+                    help="with a one-rank workload: run the pass as the per-step path a multi-GPU ring calls "
+                         "(one ra_blockwise_attn_fwd_step / _bwd_step per visible ring step, then the "
+                         "finalize calls), K/V blocks already in contiguous receive buffers (a sweep line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash and exit")
@@ -140,8 +140,8 @@ def main():
             print(f"--ring-rank needs a one-rank workload and a rank in [0, {w.n_ring})", file=sys.stderr)
             sys.exit(2)
         w = W.replace(w, ring_rank=args.ring_rank, name=f"{w.name.rsplit('-r', 1)[0]}-r{args.ring_rank}")
-    if args.ring_steps and not (args.fwd_only and w.ring_rank >= 0 and w.dtype == "bf16"):
-        print("--ring-steps needs --fwd-only and a one-rank bf16 workload", file=sys.stderr)
+    if args.ring_steps and not (w.ring_rank >= 0 and w.dtype == "bf16"):
+        print("--ring-steps needs a one-rank bf16 workload", file=sys.stderr)
         sys.exit(2)
     if not w.backward and not args.fwd_only:
         w = W.replace(w, backward=True)
@@ -156,6 +156,8 @@ def main():
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         delta = torch.empty_like(lse)
     names = ["fwd"] if args.fwd_only else ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+    if args.ring_steps and not args.fwd_only:
+        names = ["fwd", "bwd_preprocess", "bwd_steps"]
 
     if args.ring_steps:
         # the blocks a device meets, in ring order, as contiguous receive buffers; causal blocks from
@@ -168,6 +170,12 @@ def main():
         state = (torch.empty((B_, Lq_, H_, D_), dtype=torch.float32, device=dev),
                  torch.empty((B_, H_, Lq_), dtype=torch.float32, device=dev),
                  torch.empty((B_, H_, Lq_), dtype=torch.float32, device=dev))
+        if not args.fwd_only:
+            # dQ sums stay here; each block's dK / dV sums would travel on with it
+            dq_acc = torch.empty((B_, Lq_, H_, D_), dtype=torch.float32, device=dev)
+            dkv_acc = [(torch.empty_like(kb, dtype=torch.float32), torch.empty_like(vb, dtype=torch.float32))
+                       for _, kb, vb in blocks]
+            dkv_out = [(torch.empty_like(kb), torch.empty_like(vb)) for _, kb, vb in blocks]
 
     def forward():
         if not args.ring_steps:
@@ -189,6 +197,15 @@ def main():
             return
         ra.blockwise_attn_bwd_preprocess(out, t["dout"], delta=delta)
         mark(2)
+        if args.ring_steps:
+            for i_, (j, kb, vb) in enumerate(blocks):
+                ra.blockwise_attn_bwd_step(q, kb, vb, lse, delta, t["dout"], bias, seg, q_pos0=r * Lb,
+                                           kv_pos0=j * Lb, causal=w.causal, dq_acc=dq_acc, dk_acc=dkv_acc[i_][0],
+                                           dv_acc=dkv_acc[i_][1], init_dq=i_ == 0, init_dkv=True)
+            for i_ in range(len(blocks)):
+                ra.blockwise_attn_bwd_finalize(dq_acc, *dkv_acc[i_], dq=dq, dk=dkv_out[i_][0], dv=dkv_out[i_][1])
+            mark(3)
+            return
         ra.blockwise_attn_bwd_dkdv(q, k, v, lse, delta, t["dout"], bias, seg, dk=dk, dv=dv, **kw)
         mark(3)
         ra.blockwise_attn_bwd_dq(q, k, v, lse, delta, t["dout"], bias, seg, dq=dq, **kw)
@@ -220,7 +237,7 @@ def main():
     if segn is None:
         pairs *= w.batch
     fl = M.flops(pairs, w.head_dim, w.heads)
-    kernel_flops = {"fwd": fl["fwd"], "bwd_dkdv": fl["dkdv"], "bwd_dq": fl["dq"]}
+    kernel_flops = {"fwd": fl["fwd"], "bwd_dkdv": fl["dkdv"], "bwd_dq": fl["dq"], "bwd_steps": fl["dkdv"] + fl["dq"]}
     total_flops = fl["fwd"] if args.fwd_only else fl["fwd_bwd"]
     value = total_flops / (ms_step * 1e-3) / 1e12
     kernels = {}
@@ -252,7 +269,7 @@ def main():
         "config": {"workload": f"{w.name}: one device's share of a {w.kv_len}-token causal context "
                                f"(ring rank {w.ring_rank} of {w.n_ring}), {w.q_len} local queries, "
                                f"{w.heads} heads, head_dim {w.head_dim}" if w.ring_rank >= 0 else w.name,
-                   "pass": ("fwd (ring steps)" if args.ring_steps else "fwd") if args.fwd_only else "fwd+bwd",
+                   "pass": ("fwd" if args.fwd_only else "fwd+bwd") + (" (ring steps)" if args.ring_steps else ""),
                    "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim, "q_len": w.q_len,
                    "kv_len": w.kv_len, "n_ring": w.n_ring, "ring_rank": w.ring_rank, "causal": w.causal,
                    "q_chunk": w.q_chunk, "k_chunk": w.k_chunk, "bias": w.bias_len > 0,

@@ -171,6 +171,31 @@ int ra_blockwise_attn_fwd_finalize(const float* o_state, const float* m_state, c
 int ra_attn_merge(void* out_a, float* lse_a, const void* out_b, const float* lse_b, const ra_shape* shape,
                   void* stream);
 
+/*
+ * One ring step of the backward pass (the recompute policy of "RingAttention核心功能全解析",
+ * 快速上手: P is recomputed from the saved lse).  Positions, masks, bias and segment ids are as in
+ * ra_blockwise_attn_fwd_step: queries q, dout [B,Lq,H,D] at q_pos0 + i, the K/V block k, v
+ * [B,Lk,H,D] (Lk == Lq) at kv_pos0 + j.  lse [B,H,Lq] is the final lse of these queries (over
+ * the whole ring) and delta [B,H,Lq] = rowsum(dout * out) (ra_blockwise_attn_bwd_preprocess).
+ * With P = exp(scale * q k^T + bias - lse) on the visible pairs and dS = P * (dout v^T - delta),
+ * the call adds, in float32 and without the scale factor of dq and dk:
+ *   dq_acc [B,Lq,H,D] += dS k,   dk_acc [B,Lk,H,D] += dS^T q,   dv_acc [B,Lk,H,D] += P^T dout.
+ * init_dq = 1 (init_dkv = 1) starts dq_acc (dk_acc, dv_acc) at zero without reading it.  In a
+ * ring, dq_acc stays with the queries while dk_acc and dv_acc travel with their K/V block and
+ * return to its owner after the last step ("手把手拆解RingAttention", section 2).  The two
+ * kernels run in order on the stream; RA_BF16 only.
+ */
+int ra_blockwise_attn_bwd_step(const void* q, const void* k, const void* v, const float* bias,
+                               const int32_t* segment_ids, int64_t seg_len, int64_t q_pos0, int64_t kv_pos0,
+                               int32_t causal, const float* lse, const float* delta, const void* dout, float* dq_acc,
+                               float* dk_acc, float* dv_acc, int32_t init_dq, int32_t init_dkv, const ra_shape* shape,
+                               void* stream);
+
+/* Gradients from the ring-step sums: dq = scale * dq_acc [B,Lq,H,D], dk = scale * dk_acc and
+ * dv = dv_acc [B,Lk,H,D], converted to shape.dtype (scale: shape.scale, or 1/sqrt(head_dim)). */
+int ra_blockwise_attn_bwd_finalize(const float* dq_acc, const float* dk_acc, const float* dv_acc, void* dq, void* dk,
+                                   void* dv, const ra_shape* shape, void* stream);
+
 /* Description of the last error on the calling thread ("" after a success). */
 const char* ra_last_error(void);
 

@@ -16,6 +16,8 @@ from .api import (  # noqa: F401
     blockwise_attn_fwd_step,
     blockwise_attn_fwd_finalize,
     attn_merge,
+    blockwise_attn_bwd_step,
+    blockwise_attn_bwd_finalize,
     bwd_workspace_size,
     library_path,
     load_library,

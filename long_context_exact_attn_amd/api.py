@@ -57,6 +57,8 @@ def load_library():
         "ra_blockwise_attn_fwd_step": [P, P, P, P, P, I64, I64, I64, I32, P, P, P, I32, SH, P],
         "ra_blockwise_attn_fwd_finalize": [P, P, P, P, P, SH, P],
         "ra_attn_merge": [P, P, P, P, SH, P],
+        "ra_blockwise_attn_bwd_step": [P, P, P, P, P, I64, I64, I64, I32, P, P, P, P, P, P, I32, I32, SH, P],
+        "ra_blockwise_attn_bwd_finalize": [P, P, P, P, P, P, SH, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -252,6 +254,53 @@ def attn_merge(out_a, lse_a, out_b, lse_b):
     _check(lib.ra_attn_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), ctypes.byref(shape),
                              _stream(out_a.device)))
     return out_a, lse_a
+
+
+def blockwise_attn_bwd_step(q, k, v, lse, delta, dout, bias=None, segment_ids=None, *, q_pos0, kv_pos0, causal,
+                            dq_acc=None, dk_acc=None, dv_acc=None, init_dq=None, init_dkv=None, scale=None):
+    """One backward ring step (ra_blockwise_attn_bwd_step): add this K/V block's contributions to
+    the float32 sums dq_acc (of the queries q) and dk_acc, dv_acc (of the block).  A sum passed as
+    None is allocated and started at zero; init_dq / init_dkv (default: the sum was None) start a
+    given one at zero.  Returns (dq_acc, dk_acc, dv_acc)."""
+    lib = load_library()
+    _tensors(q, k, v, bias, None, extra=(("lse", lse), ("delta", delta), ("dout", dout)))
+    if segment_ids is not None and (segment_ids.dtype != torch.int32 or segment_ids.dim() != 2
+                                    or segment_ids.shape[0] != q.shape[0] or not segment_ids.is_cuda
+                                    or not segment_ids.is_contiguous()):
+        raise ValueError("segment_ids must be a contiguous int32 GPU tensor of shape [batch, seq_len]")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    i_dq = dq_acc is None if init_dq is None else bool(init_dq)
+    i_dkv = (dk_acc is None or dv_acc is None) if init_dkv is None else bool(init_dkv)
+    dq_acc = torch.empty(q.shape, **f32) if dq_acc is None else dq_acc
+    dk_acc = torch.empty(k.shape, **f32) if dk_acc is None else dk_acc
+    dv_acc = torch.empty(v.shape, **f32) if dv_acc is None else dv_acc
+    _tensors(q, k, v, None, None, extra=(("dq_acc", dq_acc), ("dk_acc", dk_acc), ("dv_acc", dv_acc)))
+    shape = make_shape(q, k, ring_rank=0, scale=scale, bias=bias)
+    seg_len = 0 if segment_ids is None else segment_ids.shape[1]
+    _check(lib.ra_blockwise_attn_bwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(seg_len),
+                                          int(q_pos0), int(kv_pos0), int(bool(causal)), _ptr(lse), _ptr(delta),
+                                          _ptr(dout), _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc), int(i_dq),
+                                          int(i_dkv), ctypes.byref(shape), _stream(q.device)))
+    return dq_acc, dk_acc, dv_acc
+
+
+def blockwise_attn_bwd_finalize(dq_acc, dk_acc, dv_acc, *, dtype=torch.bfloat16, scale=None, dq=None, dk=None,
+                                dv=None):
+    """dq, dk, dv = ra_blockwise_attn_bwd_finalize(...) from the ring-step sums."""
+    lib = load_library()
+    B, Lq, H, D = dq_acc.shape
+    Lk = dk_acc.shape[1]
+    dq = torch.empty(dq_acc.shape, dtype=dtype, device=dq_acc.device) if dq is None else dq
+    dk = torch.empty(dk_acc.shape, dtype=dtype, device=dq_acc.device) if dk is None else dk
+    dv = torch.empty(dv_acc.shape, dtype=dtype, device=dq_acc.device) if dv is None else dv
+    _tensors(dq_acc, dq_acc, dq_acc, None, None,
+             extra=(("dk_acc", dk_acc), ("dv_acc", dv_acc), ("dq", dq), ("dk", dk), ("dv", dv)))
+    if dv_acc.shape != dk_acc.shape or dq.shape != dq_acc.shape or dk.shape != dk_acc.shape or dv.shape != dk.shape:
+        raise ValueError("gradient sums and outputs must have matching shapes")
+    shape = Shape(B, H, D, -1, Lq, Lk, 0, 0.0 if scale is None else float(scale), _DTYPES[dtype])
+    _check(lib.ra_blockwise_attn_bwd_finalize(_ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc), _ptr(dq), _ptr(dk), _ptr(dv),
+                                              ctypes.byref(shape), _stream(dq_acc.device)))
+    return dq, dk, dv
 
 
 def default_scale(head_dim):

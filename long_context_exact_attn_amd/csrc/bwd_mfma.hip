@@ -25,7 +25,9 @@ namespace {
 // ================================================================== dQ (query tiles stationary)
 constexpr int kBkDq = 64;   // keys per K/V tile
 
-template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC>
+// STEP: one backward ring step (ra_blockwise_attn_bwd_step): the keys held are one block at
+// global positions kv_pos0 + j, and dQ is summed into float32 caller memory (unscaled).
+template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC, bool STEP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void dq_mfma_kernel(Params p) {
   constexpr int BK = kBkDq;
   constexpr int QW = 32 * NQB;         // queries per wave
@@ -64,13 +66,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   const int64_t qa = (t % n_qt_blk) * BQ;
   const int r = p.ring_rank < 0 ? r_local : p.ring_rank;
   const int64_t qrow_base = static_cast<int64_t>(r_local) * p.Lb;
-  const int64_t pos0 = static_cast<int64_t>(r) * p.Lb + qa;
+  // position of the tile's row 0 relative to key 0 of the keys held
+  const int64_t pos0 = (STEP ? p.q_pos0 - p.kv_pos0 : static_cast<int64_t>(r) * p.Lb) + qa;
   const int64_t nrows = (p.Lb - qa) < BQ ? (p.Lb - qa) : BQ;
 
   const __bf16* __restrict__ qp = static_cast<const __bf16*>(p.q);
   const __bf16* __restrict__ kp = static_cast<const __bf16*>(p.k);
   const __bf16* __restrict__ vp = static_cast<const __bf16*>(p.v);
   const __bf16* __restrict__ gp = static_cast<const __bf16*>(p.dout);
+  // segment ids on positions relative to the keys held (kv_pos0 = 0 outside a ring step)
+  const int* __restrict__ ids = HAS_SEG ? p.seg + static_cast<int64_t>(b) * p.seg_len + p.kv_pos0 : nullptr;
 
   const int64_t wrow0 = qa + wave * QW;
   const int64_t wpos0 = pos0 + wave * QW;
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     // rows that do not exist or see no key get P = 0 everywhere (exp2(-inf))
     lse2[nb] = (ok && L != -INFINITY) ? L * kLog2e : INFINITY;
     dlt[nb] = ok ? p.delta[li] : 0.f;
-    qseg[nb] = (HAS_SEG && ok) ? p.seg[static_cast<int64_t>(b) * p.Lk + wpos0 + nb * 32 + l32] : 0;
+    qseg[nb] = (HAS_SEG && ok) ? ids[wpos0 + nb * 32 + l32] : 0;
   }
   // the workgroup's range of query segment ids: K/V tiles with no key id in it are passed over
   int gseg_lo = 0, gseg_hi = 0;
@@ -116,6 +121,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) dQ[db][nb] = f32x16{};
+  if constexpr (STEP) {
+    if (!p.init_dq) {
+      // the sums of earlier ring steps: lane holds d = db*32 + 8*(v/4) + 4*hh + v%4 of its query
+#pragma unroll
+      for (int nb = 0; nb < NQB; ++nb) {
+        const int64_t row = wrow0 + nb * 32 + l32;
+        if (row >= p.Lb) continue;
+        const float* src = p.dq_acc + row_offset(b, row, h, p.Lq, p.H, D);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(src + db * 32 + 8 * v4 + 4 * hh);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dQ[db][nb][4 * v4 + i] = x[i];
+          }
+      }
+    }
+  }
 
   // K/V tiles: direct global -> LDS copies into a ring of NS stages, as in the forward
   const int64_t kv_bh = (static_cast<int64_t>(b) * p.Lk * p.H + h) * D;
@@ -138,8 +162,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     if (tid < BK) {
       kok = key0 + tid < kend;
       const int key = kok ? key0 + tid : key0;
-      if constexpr (HAS_BIAS) breg = p.bias[static_cast<int64_t>(h) * p.bias_len + static_cast<unsigned>(key) % static_cast<unsigned>(p.bias_len)];
-      if constexpr (HAS_SEG) sreg = p.seg[static_cast<int64_t>(b) * p.Lk + key];
+      if constexpr (HAS_BIAS)
+        breg = p.bias[static_cast<int64_t>(h) * p.bias_len +
+                      static_cast<unsigned>(static_cast<int>(p.kv_pos0) + key) % static_cast<unsigned>(p.bias_len)];
+      if constexpr (HAS_SEG) sreg = ids[key];
     }
   };
   auto store_small = [&](int slot) {
@@ -164,12 +190,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   RingWalk walk;
   walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
   SegTileFilter filt;   // with segment ids: pass over tiles sharing no id with the queries
-  const int* __restrict__ kv_ids = HAS_SEG ? p.seg + static_cast<int64_t>(b) * p.Lk : nullptr;
   auto next_tile = [&]() -> bool {
     while (walk.next<BK>()) {
       if constexpr (!HAS_SEG) return true;
       static_assert(BK == 64, "the segment filter works in 64-key tiles");
-      const int skip = filt.skip(kv_ids, walk.key0, walk.kend, gseg_lo, gseg_hi, lane);
+      const int skip = filt.skip(ids, walk.key0, walk.kend, gseg_lo, gseg_hi, lane);
       if (skip == 0) return true;
       walk.key0 += (skip - 1) * BK;   // next() adds the last BK
     }
@@ -331,6 +356,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     tke[NS - 1] = walk.kend;
   }
 
+  if constexpr (STEP) {
+    // unscaled float32 sums back to caller memory
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+      const int64_t row = wrow0 + nb * 32 + l32;
+      if (row >= p.Lb) continue;
+      float* dst = p.dq_acc + row_offset(b, row, h, p.Lq, p.H, D);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          f32x4 x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = dQ[db][nb][4 * v4 + i];
+          *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * v4 + 4 * hh) = x;
+        }
+    }
+    return;
+  }
   __bf16* __restrict__ dqp = static_cast<__bf16*>(p.dq);
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
@@ -355,7 +399,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 #endif
 constexpr int kBqKv = RA_KV_BQ;   // queries per LDS tile
 
-template <int D, int NKB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC>
+// STEP: one backward ring step (ra_blockwise_attn_bwd_step): the queries held are one block at
+// global positions q_pos0 + i, and dK / dV are summed into float32 caller memory (unscaled).
+template <int D, int NKB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC, bool STEP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void dkdv_mfma_kernel(Params p) {
   constexpr int BQ = kBqKv;
   constexpr int KW = 32 * NKB;         // keys per wave
@@ -402,6 +448,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   const __bf16* __restrict__ kp = static_cast<const __bf16*>(p.k);
   const __bf16* __restrict__ vp = static_cast<const __bf16*>(p.v);
   const __bf16* __restrict__ gp = static_cast<const __bf16*>(p.dout);
+  // segment ids on positions relative to the keys held (kv_pos0 = 0 outside a ring step)
+  const int* __restrict__ ids = HAS_SEG ? p.seg + static_cast<int64_t>(b) * p.seg_len + p.kv_pos0 : nullptr;
 
   // the wave's keys, as B operands of S = Q . K^T and dP = dO . V^T
   bf16x8 Kf[NKB][KK], Vf[NKB][KK];
@@ -420,8 +468,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       Kf[kb][kk] = ok ? x : bf16x8{};
       Vf[kb][kk] = ok ? y : bf16x8{};
     }
-    kbias[kb] = (HAS_BIAS && ok) ? p.bias[static_cast<int64_t>(h) * p.bias_len + key % p.bias_len] * kLog2e : 0.f;
-    ksg[kb] = (HAS_SEG && ok) ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
+    kbias[kb] = (HAS_BIAS && ok) ? p.bias[static_cast<int64_t>(h) * p.bias_len + (p.kv_pos0 + key) % p.bias_len] * kLog2e
+                                 : 0.f;
+    ksg[kb] = (HAS_SEG && ok) ? ids[key] : 0;
   }
   // the workgroup's range of key segment ids: query tiles with no id in it are passed over
   int gseg_lo = 0, gseg_hi = 0;
@@ -445,6 +494,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       dK[db][kb] = f32x16{};
       dV[db][kb] = f32x16{};
     }
+  if constexpr (STEP) {
+    if (!p.init_dkv) {
+      // the sums of earlier ring steps: lane holds d = db*32 + 8*(v/4) + 4*hh + v%4 of its key
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int64_t krow = wk0 + kb * 32 + l32;
+        if (krow >= p.Lb) continue;
+        const int64_t off = row_offset(b, krow, h, p.Lk, p.H, D);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(p.dk_acc + off + db * 32 + 8 * v4 + 4 * hh);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(p.dv_acc + off + db * 32 + 8 * v4 + 4 * hh);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              dK[db][kb][4 * v4 + i] = x[i];
+              dV[db][kb][4 * v4 + i] = y[i];
+            }
+          }
+      }
+    }
+  }
 
   // ---- query tile staging: direct global -> LDS copies of Q and dO into a ring of NS
   // stages, issued NS - 1 tiles ahead (rows past the rank's end fetch the tile's row 0:
@@ -475,7 +547,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       const int64_t li = (static_cast<int64_t>(b) * p.H + h) * p.Lq + rr;
       lreg = p.lse[li];
       dreg = p.delta[li];
-      if constexpr (HAS_SEG) sreg = p.seg[static_cast<int64_t>(b) * p.Lk + pbase + rr];
+      if constexpr (HAS_SEG) sreg = ids[pbase + rr];
     }
   };
   auto store_small = [&](int slot) {
@@ -500,15 +572,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 
   // query walk with NS - 1 tiles of lookahead: entry 0 is computed, entry NS - 1 is issued
   QueryWalk walk;
-  walk.begin(p.n_ring, j, p.Lb, CAUSAL, kfirst, p.ring_rank);
+  if constexpr (STEP) walk.begin_step(p.Lq, CAUSAL, kfirst, p.q_pos0 - p.kv_pos0);
+  else walk.begin(p.n_ring, j, p.Lb, CAUSAL, kfirst, p.ring_rank);
   SegTileFilter filt;   // with segment ids: pass over query tiles sharing no id with the keys
-  const int* __restrict__ q_ids = HAS_SEG ? p.seg + static_cast<int64_t>(b) * p.Lk : nullptr;
   auto next_tile = [&]() -> bool {
     while (walk.next<BQ>()) {
       if constexpr (!HAS_SEG) return true;
       static_assert(BQ == 64, "the segment filter works in 64-query tiles");
       // local rows of the current rank: the id of row q sits at position pos_base + q
-      const int skip = filt.skip(q_ids + walk.pos_base, walk.row0, walk.rend, gseg_lo, gseg_hi, lane);
+      const int skip = filt.skip(ids + walk.pos_base, walk.row0, walk.rend, gseg_lo, gseg_hi, lane);
       if (skip == 0) return true;
       walk.row0 += (skip - 1) * BQ;   // next() adds the last BQ
     }
@@ -674,6 +746,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   }
 
   // dK^T / dV^T accumulators: lane holds d = db*32 + 8*(v/4) + 4*hh + v%4 of key column l32
+  if constexpr (STEP) {
+    // unscaled float32 sums back to caller memory
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int64_t krow = wk0 + kb * 32 + l32;
+      if (krow >= p.Lb) continue;
+      const int64_t off = row_offset(b, krow, h, p.Lk, p.H, D);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          f32x4 x, y;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[i] = dK[db][kb][4 * v4 + i];
+            y[i] = dV[db][kb][4 * v4 + i];
+          }
+          *reinterpret_cast<f32x4*>(p.dk_acc + off + db * 32 + 8 * v4 + 4 * hh) = x;
+          *reinterpret_cast<f32x4*>(p.dv_acc + off + db * 32 + 8 * v4 + 4 * hh) = y;
+        }
+    }
+    return;
+  }
   __bf16* __restrict__ dkp = static_cast<__bf16*>(p.dk);
   __bf16* __restrict__ dvp = static_cast<__bf16*>(p.dv);
 #pragma unroll
@@ -711,7 +806,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   } while (0)
 
 // head_dim 64 fits two waves per SIMD without spilling; head_dim 128 keeps one
-template <int D, int NQB>
+template <int D, int NQB, bool STEP>
 hipError_t dq_d(const Params& p, hipStream_t st) {
   constexpr int OCC = D == 64 ? 2 : 1;
   constexpr int BQ = kWaves * 32 * NQB;
@@ -719,13 +814,13 @@ hipError_t dq_d(const Params& p, hipStream_t st) {
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
 #define RA_L(C, B, S) \
-  hipLaunchKernelGGL((dq_mfma_kernel<D, NQB, C, B, S, OCC>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
+  hipLaunchKernelGGL((dq_mfma_kernel<D, NQB, C, B, S, OCC, STEP>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
   RA_SELECT_FLAGS(RA_L);
 #undef RA_L
   return hipGetLastError();
 }
 
-template <int D, int NKB>
+template <int D, int NKB, bool STEP>
 hipError_t dkdv_d(const Params& p, hipStream_t st) {
   constexpr int OCC = D == 64 ? 2 : 1;
   constexpr int BKW = kWaves * 32 * NKB;
@@ -733,7 +828,7 @@ hipError_t dkdv_d(const Params& p, hipStream_t st) {
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
 #define RA_L(C, B, S) \
-  hipLaunchKernelGGL((dkdv_mfma_kernel<D, NKB, C, B, S, OCC>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
+  hipLaunchKernelGGL((dkdv_mfma_kernel<D, NKB, C, B, S, OCC, STEP>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
   RA_SELECT_FLAGS(RA_L);
 #undef RA_L
   return hipGetLastError();
@@ -742,14 +837,26 @@ hipError_t dkdv_d(const Params& p, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t st) {
-  if (p.D == 64) return dq_d<64, 1>(p, st);
-  if (p.D == 128) return dq_d<128, 1>(p, st);
+  if (p.D == 64) return dq_d<64, 1, false>(p, st);
+  if (p.D == 128) return dq_d<128, 1, false>(p, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dkdv_mfma(const Params& p, hipStream_t st) {
-  if (p.D == 64) return dkdv_d<64, 1>(p, st);
-  if (p.D == 128) return dkdv_d<128, 1>(p, st);
+  if (p.D == 64) return dkdv_d<64, 1, false>(p, st);
+  if (p.D == 128) return dkdv_d<128, 1, false>(p, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_step_mfma(const Params& p, hipStream_t st) {
+  if (p.D == 64) return dq_d<64, 1, true>(p, st);
+  if (p.D == 128) return dq_d<128, 1, true>(p, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dkdv_step_mfma(const Params& p, hipStream_t st) {
+  if (p.D == 64) return dkdv_d<64, 1, true>(p, st);
+  if (p.D == 128) return dkdv_d<128, 1, true>(p, st);
   return hipErrorInvalidValue;
 }
 

@@ -338,6 +338,84 @@ int ra_blockwise_attn_fwd_step(const void* q, const void* k, const void* v, cons
   return hip_status(ra::launch_fwd_step_mfma(c.p, static_cast<hipStream_t>(stream)), "ring step launch");
 }
 
+int ra_blockwise_attn_bwd_step(const void* q, const void* k, const void* v, const float* bias,
+                               const int32_t* segment_ids, int64_t seg_len, int64_t q_pos0, int64_t kv_pos0,
+                               int32_t causal, const float* lse, const float* delta, const void* dout, float* dq_acc,
+                               float* dk_acc, float* dv_acc, int32_t init_dq, int32_t init_dkv, const ra_shape* shape,
+                               void* stream) {
+  RA_TRY(check_dims(shape));
+  if (shape->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "ring steps are implemented for RA_BF16 only");
+  if (shape->q_len != shape->kv_len)
+    return fail(RA_ERR_SHAPE, "a ring step needs equal query and key blocks (q_len %lld, kv_len %lld)",
+                (long long)shape->q_len, (long long)shape->kv_len);
+  if (q_pos0 < 0 || kv_pos0 < 0) return fail(RA_ERR_ARG, "q_pos0 and kv_pos0 must be >= 0");
+  if (q_pos0 + shape->q_len >= kMaxPos || kv_pos0 + shape->kv_len >= kMaxPos)
+    return fail(RA_ERR_SHAPE, "global positions must stay below 2^30");
+  if ((init_dq != 0 && init_dq != 1) || (init_dkv != 0 && init_dkv != 1))
+    return fail(RA_ERR_ARG, "init_dq and init_dkv must be 0 or 1 (got %d, %d)", init_dq, init_dkv);
+  ra_shape blk = *shape;
+  blk.ring_rank = 0;   // one block each of queries and keys, causal on the global positions below
+  Checked c;
+  RA_TRY(check_shape(&blk, 1, &c));
+  RA_TRY(check_mask_args(&blk, bias, 1, 1, causal, &c));
+  RA_TRY(check_inputs(c, q, k, v, bias, segment_ids, &blk));
+  if (segment_ids) {
+    const int64_t need = (q_pos0 > kv_pos0 ? q_pos0 : kv_pos0) + shape->q_len;
+    if (seg_len < need)
+      return fail(RA_ERR_SHAPE, "segment_ids rows of %lld positions do not cover position %lld", (long long)seg_len,
+                  (long long)(need - 1));
+  }
+  RA_TRY(need_ptr(lse, c.rows, "lse", 4));
+  RA_TRY(need_ptr(delta, c.rows, "delta", 4));
+  RA_TRY(need_ptr(dout, c.q_elems, "dout", 16));
+  RA_TRY(need_ptr(dq_acc, c.q_elems, "dq_acc", 16));
+  RA_TRY(need_ptr(dk_acc, c.kv_elems, "dk_acc", 16));
+  RA_TRY(need_ptr(dv_acc, c.kv_elems, "dv_acc", 16));
+  if (c.rows == 0) return ok();
+  c.p.q = q;
+  c.p.k = k;
+  c.p.v = v;
+  c.p.bias = bias;
+  c.p.seg = segment_ids;
+  c.p.seg_len = segment_ids ? seg_len : blk.kv_len;
+  c.p.q_pos0 = q_pos0;
+  c.p.kv_pos0 = kv_pos0;
+  c.p.lse = const_cast<float*>(lse);
+  c.p.delta = delta;
+  c.p.dout = dout;
+  c.p.dq_acc = dq_acc;
+  c.p.dk_acc = dk_acc;
+  c.p.dv_acc = dv_acc;
+  c.p.init_dq = init_dq;
+  c.p.init_dkv = init_dkv;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  RA_TRY(hip_status(ra::launch_bwd_dkdv_step_mfma(c.p, st), "dK/dV ring step launch"));
+  return hip_status(ra::launch_bwd_dq_step_mfma(c.p, st), "dQ ring step launch");
+}
+
+int ra_blockwise_attn_bwd_finalize(const float* dq_acc, const float* dk_acc, const float* dv_acc, void* dq, void* dk,
+                                   void* dv, const ra_shape* shape, void* stream) {
+  RA_TRY(check_dims(shape));
+  const int64_t HB = static_cast<int64_t>(shape->batch) * shape->heads;
+  const int64_t q_elems = HB * shape->q_len * shape->head_dim;
+  const int64_t kv_elems = HB * shape->kv_len * shape->head_dim;
+  if ((q_elems / 4 + 255) / 256 > 0x7fffffffLL || (kv_elems / 4 + 255) / 256 > 0x7fffffffLL)
+    return fail(RA_ERR_SHAPE, "problem too large for one launch");
+  RA_TRY(need_ptr(dq_acc, q_elems, "dq_acc", 16));
+  RA_TRY(need_ptr(dk_acc, kv_elems, "dk_acc", 16));
+  RA_TRY(need_ptr(dv_acc, kv_elems, "dv_acc", 16));
+  const size_t el = shape->dtype == RA_BF16 ? 2 : 4;
+  RA_TRY(need_ptr(dq, q_elems, "dq", el));
+  RA_TRY(need_ptr(dk, kv_elems, "dk", el));
+  RA_TRY(need_ptr(dv, kv_elems, "dv", el));
+  const float scale = shape->scale > 0.f ? shape->scale : 1.0f / std::sqrt(static_cast<float>(shape->head_dim));
+  const bool bf16 = shape->dtype == RA_BF16;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  RA_TRY(hip_status(ra::launch_grad_finalize(dq_acc, scale, dq, q_elems, bf16, st), "dQ finalize launch"));
+  RA_TRY(hip_status(ra::launch_grad_finalize(dk_acc, scale, dk, kv_elems, bf16, st), "dK finalize launch"));
+  return hip_status(ra::launch_grad_finalize(dv_acc, 1.0f, dv, kv_elems, bf16, st), "dV finalize launch");
+}
+
 int ra_blockwise_attn_fwd_finalize(const float* o_state, const float* m_state, const float* l_state, void* out,
                                    float* lse, const ra_shape* shape, void* stream) {
   RA_TRY(check_dims(shape));

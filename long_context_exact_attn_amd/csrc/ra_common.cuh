@@ -52,6 +52,12 @@ struct Params {
   float* m_state;           // [B, H, Lq] reference maximum, log2 units
   float* l_state;           // [B, H, Lq] sum of exponentials against m_state
   int32_t step_init;        // 1: start from an empty state (the incoming one is not read)
+  // one backward ring step (ra_blockwise_attn_bwd_step): unscaled float32 gradient sums in
+  // caller memory, dQ for the queries held, dK / dV for the K/V block held
+  float* dq_acc;            // [B, Lq, H, D]
+  float* dk_acc;            // [B, Lk, H, D]
+  float* dv_acc;            // [B, Lk, H, D]
+  int32_t init_dq, init_dkv;   // 1: the sums start at zero (the incoming ones are not read)
 };
 
 // ---------------------------------------------------------------- element access
@@ -112,10 +118,19 @@ struct QueryWalk {
   int row0, rend, rstop;   // local query rows [row0, row0+BQ) of q; rend: end of the rank's rows
   int pos_base;            // global position of local row 0 of the current rank
   int cur_rank;
+  bool step;               // one ring step: one query block, positions relative to the keys held
+  int step_off;            // ... its row 0's position relative to key 0 of the block held
   __device__ void begin(int n_, int j_, int64_t Lb_, bool causal_, int64_t kfirst_, int rank_only_) {
     n = n_; j = j_; Lb = static_cast<int>(Lb_); causal = causal_; kfirst = static_cast<int>(kfirst_);
     rank_only = rank_only_;
     s = -1; row0 = 0; rend = 0; rstop = 0; pos_base = 0; cur_rank = 0;
+    step = false; step_off = 0;
+  }
+  // one ring step: rows [0, Lq) of the query block, at positions off + row relative to the keys
+  __device__ void begin_step(int64_t Lq_, bool causal_, int64_t kfirst_, int64_t off) {
+    begin(1, 0, Lq_, causal_, kfirst_, 0);
+    step = true;
+    step_off = static_cast<int>(off);
   }
   template <int BQ>
   __device__ bool next() {
@@ -126,13 +141,13 @@ struct QueryWalk {
       int r = j + s;
       if (r >= n) r -= n;
       if (rank_only >= 0 && r != rank_only) continue;
-      if (causal && r < j) continue;        // queries before the block see none of it
+      if (!step && causal && r < j) continue;   // queries before the block see none of it
       cur_rank = r;
       const int local0 = rank_only >= 0 ? 0 : r * Lb;   // first local row of rank r
-      pos_base = r * Lb - local0;                       // global pos = local row + pos_base
+      pos_base = step ? step_off : r * Lb - local0;     // global pos = local row + pos_base
       rend = local0 + Lb;
       row0 = local0;
-      if (causal && r == j) {
+      if (causal && (step || r == j)) {
         // skip whole query tiles that end before kfirst: first row with pos >= kfirst
         const int first_row = kfirst - pos_base;
         if (first_row > row0) row0 += ((first_row - row0) / BQ) * BQ;
@@ -154,5 +169,8 @@ hipError_t launch_bwd_dkdv_simt(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dq_simt(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dkdv_mfma(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t st);
+hipError_t launch_bwd_dkdv_step_mfma(const Params& p, hipStream_t st);
+hipError_t launch_bwd_dq_step_mfma(const Params& p, hipStream_t st);
+hipError_t launch_grad_finalize(const float* acc, float factor, void* out, int64_t elems, bool bf16, hipStream_t st);
 
 }  // namespace ra

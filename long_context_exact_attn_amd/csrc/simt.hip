@@ -464,6 +464,27 @@ hipError_t launch_merge_t(const Params& p, const void* out_b, const float* lse_b
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
+// factor * acc converted to the output type, four elements per lane (the row length is a
+// multiple of 4, so the element count is too)
+template <typename T>
+__global__ __launch_bounds__(256) void grad_finalize_kernel(const float* __restrict__ acc, float factor,
+                                                            T* __restrict__ out, int64_t n4) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4 x = reinterpret_cast<const f32x4*>(acc)[i];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[4 * i + e] = from_f32<T>(x[e] * factor);
+}
+
+hipError_t launch_grad_finalize(const float* acc, float factor, void* out, int64_t elems, bool bf16, hipStream_t st) {
+  const int64_t n4 = elems / 4;
+  if (n4 == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((n4 + 255) / 256));
+  if (bf16) hipLaunchKernelGGL(grad_finalize_kernel<__bf16>, grid, dim3(256), 0, st, acc, factor, static_cast<__bf16*>(out), n4);
+  else hipLaunchKernelGGL(grad_finalize_kernel<float>, grid, dim3(256), 0, st, acc, factor, static_cast<float*>(out), n4);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_finalize(const Params& p, hipStream_t st) {
   return p.bf16 ? launch_finalize_t<__bf16>(p, st) : launch_finalize_t<float>(p, st);
 }

@@ -189,3 +189,31 @@ def test_positions_must_fit_32_bits():
     assert rc == -2 and b"2^30" in lib.ra_last_error()
     s = api.Shape(1, 2, 64, -1, 512, 512, 1 << 30, 0.0, api.RA_BF16)
     assert _fwd(lib, s, n_ring=1, q_chunk=512, k_chunk=512, bias=FAKE) == -1
+
+
+@needs_cpu
+def test_bwd_step_validation():
+    lib = _lib()
+    S = lambda **kw: api.Shape(**{**dict(batch=1, heads=2, head_dim=64, ring_rank=-1, q_len=512, kv_len=512,  # noqa
+                                         bias_len=0, scale=0.0, dtype=api.RA_BF16), **kw})
+
+    def step(shape, seg=None, seg_len=0, q_pos0=512, kv_pos0=0, i_dq=1, i_dkv=1, dv=None, delta=FAKE):
+        return lib.ra_blockwise_attn_bwd_step(FAKE, FAKE, FAKE, None, seg, seg_len, q_pos0, kv_pos0, 1, FAKE, delta,
+                                              FAKE, FAKE, FAKE, dv, i_dq, i_dkv, ctypes.byref(shape), None)
+
+    # dv_acc stays NULL in every call: none can reach a launch
+    assert step(S(kv_len=256)) == -2 and b"equal query and key" in lib.ra_last_error()
+    assert step(S(dtype=api.RA_F32)) == -3
+    assert step(S(), kv_pos0=-1) == -1
+    assert step(S(), q_pos0=(1 << 30) - 10) == -2
+    assert step(S(), i_dkv=3) == -1
+    assert step(S(), seg=FAKE, seg_len=600) == -2 and b"do not cover" in lib.ra_last_error()
+    assert step(S(), delta=None) == -1 and b"delta" in lib.ra_last_error()
+    assert step(S()) == -1 and b"dv_acc" in lib.ra_last_error()
+    assert step(S(batch=0)) == 0
+
+    s = S()
+    rc = lib.ra_blockwise_attn_bwd_finalize(FAKE, FAKE, FAKE, FAKE, FAKE, None, ctypes.byref(s), None)
+    assert rc == -1 and b"dv" in lib.ra_last_error()
+    rc = lib.ra_blockwise_attn_bwd_finalize(FAKE, FAKE, FAKE, FAKE, FAKE, None, ctypes.byref(S(head_dim=72)), None)
+    assert rc == -3

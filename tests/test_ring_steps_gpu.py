@@ -149,3 +149,81 @@ def test_step_errors(gpu):
     qf = t["q"].float()
     with pytest.raises(ra.RAError, match="RA_BF16"):
         ra.blockwise_attn_fwd_step(qf, qf, qf, q_pos0=0, kv_pos0=0, causal=True)
+
+
+# ------------------------------------------------------------------ backward ring steps
+def _ring_backward(w, t, out, lse, skip_future=True):
+    """All ranks of a ring on one GPU, one ra_blockwise_attn_bwd_step per (rank, step): dQ sums
+    stay with each rank's queries, dK / dV sums travel with their block."""
+    n, lb = w.n_ring, w.block_len
+    delta = ra.blockwise_attn_bwd_preprocess(out, t["dout"])
+    dq_acc = [None] * n
+    dkv_acc = [None] * n
+    for r in range(n):
+        rows = slice(r * lb, (r + 1) * lb)
+        q_r, g_r = t["q"][:, rows].contiguous(), t["dout"][:, rows].contiguous()
+        lse_r, dl_r = lse[:, :, rows].contiguous(), delta[:, :, rows].contiguous()
+        for s in range(n):
+            j = (r - s) % n
+            if skip_future and w.causal and j > r:
+                continue
+            kb, vb = _block(t["k"], j, lb), _block(t["v"], j, lb)
+            dk_a, dv_a = dkv_acc[j] if dkv_acc[j] is not None else (None, None)
+            dq_acc[r], dk_a, dv_a = ra.blockwise_attn_bwd_step(
+                q_r, kb, vb, lse_r, dl_r, g_r, t["bias"], t["segment_ids"], q_pos0=r * lb, kv_pos0=j * lb,
+                causal=w.causal, dq_acc=dq_acc[r], dk_acc=dk_a, dv_acc=dv_a)
+            dkv_acc[j] = (dk_a, dv_a)
+    grads = [ra.blockwise_attn_bwd_finalize(dq_acc[i], *dkv_acc[i]) for i in range(n)]
+    dq = torch.cat([g[0] for g in grads], dim=1)
+    dk = torch.cat([g[1] for g in grads], dim=1)
+    dv = torch.cat([g[2] for g in grads], dim=1)
+    return dq, dk, dv
+
+
+BWD_CASES = [
+    ("causal-ring4", dict(kv_len=2048, n_ring=4)),
+    ("noncausal-bias-seg", dict(kv_len=1536, n_ring=3, causal=False, bias_len=100, segments="docs", doc_len=(20, 400))),
+    ("ragged-250", dict(kv_len=1000, n_ring=4, segments="scattered")),
+    ("d128-batch2", dict(head_dim=128, batch=2, heads=3, kv_len=1024, n_ring=2, bias_len=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_bwd_step_ring_matches_oracle_and_fused(gpu, name, kw):
+    w = W.small(name, backward=True, **kw)
+    t = P.make(w, gpu)
+    out, lse = P.gpu_forward(w, t)
+    dq, dk, dv = _ring_backward(w, t, out, lse)
+    fq, fk, fv = P.gpu_backward(w, t, out, lse)
+    torch.cuda.synchronize()
+    d = P.oracle_inputs(t)
+    import oracle
+    rdq, rdk, rdv, _ = oracle.backward(d["q"], d["k"], d["v"], d["dout"], q_pos=w.q_positions(), causal=w.causal,
+                                       bias=d["bias"], segment_ids=d["segment_ids"])
+    for gname, g, f, r in (("dq", dq, fq, rdq), ("dk", dk, fk, rdk), ("dv", dv, fv, rdv)):
+        P.assert_close(f"{name} {gname} steps vs oracle", P.np64(g), r, "bf16", strict=False)
+        P.assert_close(f"{name} {gname} steps vs fused", P.np64(g), P.np64(f), "bf16", strict=False)
+
+
+def test_bwd_step_future_block_is_a_no_op(gpu):
+    w = W.small("bwd-future", backward=True, kv_len=2048, n_ring=4, bias_len=64, segments="docs", doc_len=(30, 300))
+    t = P.make(w, gpu)
+    out, lse = P.gpu_forward(w, t)
+    a = _ring_backward(w, t, out, lse, skip_future=True)
+    b = _ring_backward(w, t, out, lse, skip_future=False)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_step_errors(gpu):
+    w = W.small("bwd-err", kv_len=1024, n_ring=2, ring_rank=1, backward=True)
+    t = P.make(w, gpu)
+    k = _block(t["k"], 0, w.block_len)
+    lse = torch.zeros(1, 2, 512, device=gpu)
+    with pytest.raises(ra.RAError, match="equal query and key blocks"):
+        ra.blockwise_attn_bwd_step(t["q"], k[:, :256].contiguous(), k[:, :256].contiguous(), lse, lse, t["dout"],
+                                   q_pos0=512, kv_pos0=0, causal=True)
+    qf = t["q"].float()
+    with pytest.raises(ra.RAError, match="RA_BF16"):
+        ra.blockwise_attn_bwd_step(qf, qf, qf, lse, lse, qf, q_pos0=0, kv_pos0=0, causal=True)
