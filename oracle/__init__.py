@@ -30,5 +30,5 @@ Parity status: every function here is pinned by CPU tests (brute force,
 library special case, closed forms, finite differences, invariants); none is
 "parity unpinned".
 """
-from .attention import forward, backward, probabilities, query_positions, visible_pairs  # noqa: F401
+from .attention import forward, backward, probabilities, query_positions, visible_pairs, causal_block  # noqa: F401
 from .blockwise import ring_forward  # noqa: F401

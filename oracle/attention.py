@@ -10,7 +10,7 @@ Definition (exact full attention; "手把手拆解RingAttention" section 1 says
 the ring keeps the whole attention map, so the result must equal plain
 attention over all keys):
 
-    visible(i, j) = (not causal or j <= p_i) and (seg is None or seg[j] == seg[p_i])
+    visible(i, j) = (not causal or j // c <= p_i // c) and (seg is None or seg[j] == seg[p_i])
     s_ij  = scale * <q_i, k_j> + bias[h, j mod bias_len]
     lse_i = log sum_{visible j} exp(s_ij)
     P_ij  = exp(s_ij - lse_i) if visible else 0
@@ -18,9 +18,14 @@ attention over all keys):
 
 ``p_i`` is the global sequence position of local query ``i``: on ring rank
 ``r`` of a ring of ``n`` blocks of ``Lb`` tokens it is ``r*Lb + i``.  The
-causal mask ("causal_block_size=1", i.e. token granularity, section
-"分块注意力计算" of the wmrh.cn page) compares *global* positions.  A row with
-no visible key has out = 0 and lse = -inf.
+causal mask compares *global* positions.  Its granularity is the page's
+``causal_block_size`` c (section "分块注意力计算" of the wmrh.cn page, where
+c = 1 turns on causal attention): the page gives no other value a meaning,
+and the reading taken is that positions fall into consecutive blocks of c
+tokens and a key is visible when its block does not come after the query's
+block.  c = 1 is token-level causal attention (j <= p_i).  ``causal`` below is
+False / 0 (no mask), True (c = 1) or the integer c.  A row with no visible
+key has out = 0 and lse = -inf.
 
 Backward (recompute policy ``nothing_saveable``, section "快速上手"), given dO:
 
@@ -57,12 +62,25 @@ def query_positions(q_len, kv_len, n_ring, ring_rank):
     return ring_rank * block + np.arange(q_len, dtype=np.int64)
 
 
+def causal_block(causal):
+    """The causal block size c of a ``causal`` argument: 0 for none, 1 for True."""
+    if causal is None or causal is False:
+        return 0
+    if causal is True:
+        return 1
+    c = int(causal)
+    if c < 0:
+        raise ValueError("causal block size must be >= 0")
+    return c
+
+
 def _visible(q_pos, kv_len, causal, seg_row):
     """Boolean [nq, kv_len]: which keys each query may attend to."""
     j = np.arange(kv_len, dtype=np.int64)
     vis = np.ones((len(q_pos), kv_len), dtype=bool)
-    if causal:
-        vis &= j[None, :] <= q_pos[:, None]
+    c = causal_block(causal)
+    if c:
+        vis &= (j // c)[None, :] <= (q_pos // c)[:, None]
     if seg_row is not None:
         seg_row = np.asarray(seg_row)
         vis &= seg_row[None, :] == seg_row[q_pos][:, None]
@@ -192,14 +210,20 @@ def visible_pairs(q_pos, kv_len, causal, segment_ids=None):
     it when causal).
     """
     q_pos = np.asarray(q_pos, dtype=np.int64)
+    c = causal_block(causal)
     if segment_ids is None:
-        if causal:
-            return int(np.sum(np.minimum(q_pos + 1, kv_len)))
+        if c:
+            # keys up to the end of the query's causal block
+            return int(np.sum(np.minimum((q_pos // c + 1) * c, kv_len)))
         return int(len(q_pos) * kv_len)
     total = 0
     for row in np.asarray(segment_ids):
         row = np.asarray(row, dtype=np.int64)
-        if causal:
+        if c > 1:
+            # per query: keys of its segment that end no later than its causal block
+            lim = np.minimum((q_pos // c + 1) * c, kv_len)
+            total += int(sum(int(np.count_nonzero(row[:lim_i] == row[p])) for p, lim_i in zip(q_pos, lim)))
+        elif c:
             # count j <= p with row[j] == row[p]: rank of p among equal ids
             order = np.argsort(row, kind="stable")
             rank = np.empty(kv_len, dtype=np.int64)

@@ -26,6 +26,8 @@ import math
 
 import numpy as np
 
+from .attention import causal_block
+
 
 def ring_forward(q, k, v, *, n_ring, ring_rank, q_chunk, k_chunk, causal, scale=None,
                  bias=None, segment_ids=None, order=None):
@@ -43,6 +45,7 @@ def ring_forward(q, k, v, *, n_ring, ring_rank, q_chunk, k_chunk, causal, scale=
         raise ValueError("ring not closed: kv_len is not n_ring * block length")
     Lb = Lk // n_ring
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    cb = causal_block(causal)   # causal block size (0: no causal mask), as in the plain definition
     if ring_rank is None or ring_rank < 0:
         if Lq != Lk:
             raise ValueError("all-ranks mode needs Lq == Lk")
@@ -76,8 +79,8 @@ def ring_forward(q, k, v, *, n_ring, ring_rank, q_chunk, k_chunk, causal, scale=
                             if bias is not None:
                                 s = s + np.asarray(bias, dtype=np.float64)[h, kpos % bias.shape[1]][None, :]
                             vis = np.ones(s.shape, dtype=bool)
-                            if causal:
-                                vis &= kpos[None, :] <= pos[:, None]
+                            if cb:
+                                vis &= (kpos // cb)[None, :] <= (pos // cb)[:, None]
                             if seg is not None:
                                 vis &= seg[kpos][None, :] == seg[pos][:, None]
                             s = np.where(vis, s, -np.inf)

@@ -83,8 +83,9 @@ def _brute(q, k, v, pos, causal, scale, bias, seg, b, h):
     outs, lses = [], []
     for i in range(Lq):
         logits = {}
+        c = 1 if causal is True else int(causal)   # causal block size (0: no mask)
         for j in range(Lk):
-            if causal and j > pos[i]:
+            if c and j // c > pos[i] // c:   # the key's block comes after the query's
                 continue
             if seg is not None and seg[b][j] != seg[b][pos[i]]:
                 continue
@@ -105,7 +106,7 @@ def _brute(q, k, v, pos, causal, scale, bias, seg, b, h):
 
 
 @pytest.mark.parametrize("ring_rank", [-1, 0, 2])
-@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("causal", [False, True, 3, 8])
 @pytest.mark.parametrize("bias_len,seg", [(0, False), (5, False), (0, True), (4, True)])
 def test_brute_force(ring_rank, causal, bias_len, seg):
     q, k, v, bias, segs, pos = _rand_case(ring_rank=ring_rank, bias_len=bias_len, seg=seg,
@@ -359,3 +360,38 @@ def test_visible_pairs_counts():
         brute = sum(int(((seg[b] == seg[b][i]) & ((np.arange(L) <= i) | (not causal))).sum())
                     for b in range(2) for i in range(L))
         assert A.visible_pairs(np.arange(L), L, causal=causal, segment_ids=seg) == brute
+
+
+def test_visible_pairs_counts_causal_blocks():
+    L = 40
+    # blocks of 8: a query sees every key up to the end of its block
+    assert A.visible_pairs(np.arange(L), L, causal=8) == sum(8 * (i // 8 + 1) for i in range(L))
+    assert A.visible_pairs(np.arange(L), L, causal=1) == L * (L + 1) // 2
+    assert A.visible_pairs(np.arange(L), L, causal=L) == L * L
+    # blocks that do not divide the length: the last one is cut at L
+    assert A.visible_pairs(np.arange(L), L, causal=16) == 16 * 16 + 16 * 32 + 8 * 40
+    seg = np.random.default_rng(6).integers(0, 3, size=(2, L))
+    for c in (2, 5, 16):
+        brute = sum(int(((seg[b] == seg[b][i]) & (np.arange(L) // c <= i // c)).sum()) for b in range(2)
+                    for i in range(L))
+        assert A.visible_pairs(np.arange(L), L, causal=c, segment_ids=seg) == brute
+
+
+def test_causal_block_one_is_token_causal():
+    q, k, v, bias, segs, pos = _rand_case(ring_rank=1, bias_len=5, seg=True, seed=21)
+    a = oracle.forward(q, k, v, q_pos=pos, causal=True, bias=bias, segment_ids=segs)
+    b = oracle.forward(q, k, v, q_pos=pos, causal=1, bias=bias, segment_ids=segs)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_ring_forward_causal_blocks():
+    # the method's own procedure with a causal block size gives the plain definition's result
+    q, k, v, bias, segs, pos = _rand_case(ring_rank=-1, bias_len=7, seg=True, seed=22)
+    n = 4
+    for c in (2, 4):
+        o, l_ = oracle.ring_forward(q, k, v, n_ring=n, ring_rank=-1, q_chunk=2, k_chunk=4, causal=c, bias=bias,
+                                    segment_ids=segs)
+        ro, rl = oracle.forward(q, k, v, q_pos=pos, causal=c, bias=bias, segment_ids=segs)
+        np.testing.assert_allclose(o, ro, atol=1e-12)
+        np.testing.assert_allclose(l_, rl, atol=1e-12)

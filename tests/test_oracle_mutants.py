@@ -20,9 +20,12 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 SRC = open(ATT.__file__).read()
 
 MUTANTS = {
-    "causal_strict": ("vis &= j[None, :] <= q_pos[:, None]", "vis &= j[None, :] < q_pos[:, None]"),
-    "causal_local_index": ("vis &= j[None, :] <= q_pos[:, None]",
-                           "vis &= j[None, :] <= np.arange(len(q_pos))[:, None]"),
+    "causal_strict": ("vis &= (j // c)[None, :] <= (q_pos // c)[:, None]", "vis &= (j // c)[None, :] < (q_pos // c)[:, None]"),
+    "causal_local_index": ("vis &= (j // c)[None, :] <= (q_pos // c)[:, None]",
+                           "vis &= (j // c)[None, :] <= (np.arange(len(q_pos)) // c)[:, None]"),
+    "causal_block_ignored": ("vis &= (j // c)[None, :] <= (q_pos // c)[:, None]", "vis &= j[None, :] <= q_pos[:, None]"),
+    "causal_block_ceil": ("vis &= (j // c)[None, :] <= (q_pos // c)[:, None]",
+                          "vis &= ((j + c - 1) // c)[None, :] <= (q_pos // c)[:, None]"),
     "segment_local_index": ("vis &= seg_row[None, :] == seg_row[q_pos][:, None]",
                             "vis &= seg_row[None, :] == seg_row[np.arange(len(q_pos))][:, None]"),
     "bias_dropped": ("        s = s + bias_row[None, :]", "        s = s"),
@@ -120,7 +123,25 @@ def pin_gradient_invariants(M):
     np.testing.assert_allclose(np.einsum("blhd,blhd->bh", dq, q), np.einsum("blhd,blhd->bh", dk, k), atol=1e-12)
 
 
-PINS = [pin_worked_examples, pin_zero_keys_per_rank, pin_sdpa, pin_gradient_invariants]
+def pin_causal_blocks(M):
+    # causal block size c: the rows of causal block b equal unmasked attention over the keys of
+    # blocks 0..b (a formulation that never touches the causal code); c >= L is no mask at all
+    rng = np.random.default_rng(8)
+    L, c = 12, 4
+    q, k, v = (rng.standard_normal((1, L, 2, 3)) for _ in range(3))
+    out, lse = M.forward(q, k, v, q_pos=np.arange(L), causal=c, scale=0.7)
+    for b in range(L // c):
+        rows, keys = slice(b * c, (b + 1) * c), slice(0, (b + 1) * c)
+        o_b, l_b = M.forward(q[:, rows], k[:, keys], v[:, keys], q_pos=np.arange(b * c, (b + 1) * c), causal=False,
+                             scale=0.7)
+        np.testing.assert_allclose(out[:, rows], o_b, atol=1e-13)
+        np.testing.assert_allclose(lse[:, :, rows], l_b, atol=1e-13)
+    o_all, _ = M.forward(q, k, v, q_pos=np.arange(L), causal=False, scale=0.7)
+    np.testing.assert_allclose(M.forward(q, k, v, q_pos=np.arange(L), causal=L, scale=0.7)[0], o_all, atol=1e-13)
+    assert M.visible_pairs(np.arange(L), L, c) == sum((p // c + 1) * c for p in range(L))
+
+
+PINS = [pin_worked_examples, pin_zero_keys_per_rank, pin_sdpa, pin_gradient_invariants, pin_causal_blocks]
 
 
 def test_pins_pass_on_the_oracle():
