@@ -15,7 +15,8 @@
  *
  * For query i with global position p_i and key j of the same batch row and
  * head:
- *   visible(i,j) = (!causal || j <= p_i) && (segment_ids == NULL || seg[j] == seg[p_i])
+ *   visible(i,j) = (!causal || j / c <= p_i / c) && (segment_ids == NULL || seg[j] == seg[p_i])
+ * with c = causal (the causal block size; integer division).
  *   s_ij   = scale * <q_i, k_j> + (bias ? bias[h, j mod bias_len] : 0)
  *   lse_i  = log sum_{visible j} exp(s_ij)            (natural log; -inf if none)
  *   out_i  = sum_{visible j} exp(s_ij - lse_i) v_j    (0 if none)
@@ -43,8 +44,13 @@
  *    each must be >= 1 and divide Lb.  The kernels' own tiles nest inside
  *    any such chunking and masked keys contribute exact zeros, so results do
  *    not depend on the chunk sizes at all.
- *  - causal is 0 or 1 (1 = causal_block_size 1, token granularity, on
- *    global positions).  Fully masked K/V tiles are skipped.
+ *  - causal is 0 (no mask) or the causal block size c in [1, 2^30): the
+ *    page's causal_block_size, where 1 turns on (token-level) causal
+ *    attention.  For c > 1 the reading taken is block-granular causality:
+ *    positions fall into consecutive blocks of c tokens and a key is visible
+ *    when its block does not come after the query's (j / c <= p_i / c, on
+ *    global positions).  c must divide the ring block length Lb.  Fully
+ *    masked K/V blocks and tiles are skipped.
  *  - dtype: RA_BF16 (inputs/outputs bfloat16, float32 accumulation, P
  *    rounded to bfloat16 before the P.V product) or RA_F32 (float32
  *    throughout).  head_dim must be 64 or 128.
@@ -70,7 +76,7 @@ typedef enum ra_dtype { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
 
 typedef enum ra_status {
   RA_OK = 0,
-  RA_ERR_ARG = -1,          /* null pointer, causal not 0/1, bad chunk, bad rank */
+  RA_ERR_ARG = -1,          /* null pointer, bad causal block size, bad chunk, bad rank */
   RA_ERR_SHAPE = -2,        /* ring does not close, Lq inconsistent with ring_rank, negative size */
   RA_ERR_UNSUPPORTED = -3,  /* head_dim or dtype the kernels do not implement */
   RA_ERR_WORKSPACE = -4,    /* workspace missing or too small */

@@ -76,6 +76,15 @@ def load_library():
     return lib
 
 
+def _causal(causal):
+    """The C ABI's causal argument: 0 (False / None), 1 (True) or a causal block size c >= 1."""
+    if causal is None or causal is False:
+        return 0
+    if causal is True:
+        return 1
+    return int(causal)
+
+
 def _check(rc):
     if rc != 0:
         raise RAError(rc, _LIB.ra_last_error().decode())
@@ -130,7 +139,7 @@ def blockwise_attn_fwd(q, k, v, bias=None, segment_ids=None, *, n_ring, q_chunk,
         lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
     _tensors(q, k, v, None, None, extra=(("out", out), ("lse", lse)))
     _check(lib.ra_blockwise_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(n_ring),
-                                     int(q_chunk), int(k_chunk), int(bool(causal)), _ptr(out), _ptr(lse),
+                                     int(q_chunk), int(k_chunk), _causal(causal), _ptr(out), _ptr(lse),
                                      ctypes.byref(shape), _stream(q.device)))
     return out, lse
 
@@ -154,7 +163,7 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, bias=None, segment_ids=None, *, 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib.ra_blockwise_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(n_ring),
-                                     int(q_chunk), int(k_chunk), int(bool(causal)), _ptr(out), _ptr(lse),
+                                     int(q_chunk), int(k_chunk), _causal(causal), _ptr(out), _ptr(lse),
                                      _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), ctypes.byref(shape),
                                      _stream(q.device)))
@@ -182,7 +191,7 @@ def blockwise_attn_bwd_dkdv(q, k, v, lse, delta, dout, bias=None, segment_ids=No
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     _check(lib.ra_blockwise_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(n_ring),
-                                          int(q_chunk), int(k_chunk), int(bool(causal)), _ptr(lse), _ptr(delta),
+                                          int(q_chunk), int(k_chunk), _causal(causal), _ptr(lse), _ptr(delta),
                                           _ptr(dout), _ptr(dk), _ptr(dv), ctypes.byref(shape), _stream(q.device)))
     return dk, dv
 
@@ -194,7 +203,7 @@ def blockwise_attn_bwd_dq(q, k, v, lse, delta, dout, bias=None, segment_ids=None
     shape = make_shape(q, k, ring_rank=ring_rank, scale=scale, bias=bias)
     dq = torch.empty_like(q) if dq is None else dq
     _check(lib.ra_blockwise_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(n_ring),
-                                        int(q_chunk), int(k_chunk), int(bool(causal)), _ptr(lse), _ptr(delta),
+                                        int(q_chunk), int(k_chunk), _causal(causal), _ptr(lse), _ptr(delta),
                                         _ptr(dout), _ptr(dq), ctypes.byref(shape), _stream(q.device)))
     return dq
 
@@ -224,7 +233,7 @@ def blockwise_attn_fwd_step(q, k, v, bias=None, segment_ids=None, *, q_pos0, kv_
     shape = make_shape(q, k, ring_rank=0, scale=scale, bias=bias)
     seg_len = 0 if segment_ids is None else segment_ids.shape[1]
     _check(lib.ra_blockwise_attn_fwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(seg_len),
-                                          int(q_pos0), int(kv_pos0), int(bool(causal)), _ptr(o), _ptr(m), _ptr(l_),
+                                          int(q_pos0), int(kv_pos0), _causal(causal), _ptr(o), _ptr(m), _ptr(l_),
                                           int(init), ctypes.byref(shape), _stream(q.device)))
     return state
 
@@ -278,7 +287,7 @@ def blockwise_attn_bwd_step(q, k, v, lse, delta, dout, bias=None, segment_ids=No
     shape = make_shape(q, k, ring_rank=0, scale=scale, bias=bias)
     seg_len = 0 if segment_ids is None else segment_ids.shape[1]
     _check(lib.ra_blockwise_attn_bwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(seg_len),
-                                          int(q_pos0), int(kv_pos0), int(bool(causal)), _ptr(lse), _ptr(delta),
+                                          int(q_pos0), int(kv_pos0), _causal(causal), _ptr(lse), _ptr(delta),
                                           _ptr(dout), _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc), int(i_dq),
                                           int(i_dkv), ctypes.byref(shape), _stream(q.device)))
     return dq_acc, dk_acc, dv_acc

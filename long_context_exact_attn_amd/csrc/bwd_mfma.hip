@@ -27,8 +27,11 @@ constexpr int kBkDq = 64;   // keys per K/V tile
 
 // STEP: one backward ring step (ra_blockwise_attn_bwd_step): the keys held are one block at
 // global positions kv_pos0 + j, and dQ is summed into float32 caller memory (unscaled).
-template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC, bool STEP>
+// CM: causal mode, 0 none, 1 token level, 2 causal blocks of p.causal > 1 tokens.
+template <int D, int NQB, int CM, bool HAS_BIAS, bool HAS_SEG, int OCC, bool STEP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void dq_mfma_kernel(Params p) {
+  constexpr bool CAUSAL = CM != 0;
+  constexpr bool CBLK = CM == 2;
   constexpr int BK = kBkDq;
   constexpr int QW = 32 * NQB;         // queries per wave
   constexpr int BQ = kWaves * QW;      // queries per workgroup
@@ -187,8 +190,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     }
   };
 
+  // causal limits: relative positions have their origin at global position kv_pos0 (0 outside a
+  // ring step); the walk stops after the last key the workgroup's last query can see
+  const int coff = static_cast<int>(p.kv_pos0);
   RingWalk walk;
-  walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
+  walk.begin(p.n_ring, r, p.Lb, CAUSAL,
+             CBLK && nrows > 0 ? causal_last_key(static_cast<int>(pos0 + nrows - 1), coff, p.causal) : pos0 + nrows - 1);
   SegTileFilter filt;   // with segment ids: pass over tiles sharing no id with the queries
   auto next_tile = [&]() -> bool {
     while (walk.next<BK>()) {
@@ -222,6 +229,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   // are below 2^30, checked on the host), so that per-tile tests stay on the scalar unit
   const int wpos = static_cast<int>(wpos0);
   const int wlast = static_cast<int>(wvalid < QW ? wvalid : QW) - 1;
+  // the last key the wave's first and last query can see, and each lane's own limits
+  int wlim_first = 0, wlim_last = 0;
+  int qlim[NQB];
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) qlim[nb] = 0;
+  if constexpr (CBLK) {
+    wlim_first = causal_last_key(wpos, coff, p.causal);
+    wlim_last = wlast >= 0 ? causal_last_key(wpos + wlast, coff, p.causal) : -1;
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) qlim[nb] = causal_last_key(wpos + nb * 32 + l32, coff, p.causal);
+  }
   int slot = 0;
   while (tok[0]) {
     const int key0 = tk0[0], kend = tke[0];
@@ -235,7 +253,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 
     const __bf16* Kt = sK[buf];
     const __bf16* Vt = sV[buf];
-    const bool wave_active = wlast >= 0 && !(CAUSAL && key0 > wpos + wlast);
+    const bool wave_active = wlast >= 0 && !(CAUSAL && key0 > (CBLK ? wlim_last : wpos + wlast));
     if (wave_active) {
       f32x16 S[2][NQB], G[2][NQB];
 #pragma unroll
@@ -263,7 +281,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       }
       __builtin_amdgcn_s_setprio(0);
 
-      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > wpos);
+      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > (CBLK ? wlim_first : wpos));
       int kseg[2][16];
       if constexpr (HAS_SEG) {
 #pragma unroll
@@ -285,7 +303,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         if (need_mask) {
           klim = (kend - key0 < BK ? kend - key0 : BK) - 1;
           if constexpr (CAUSAL) {
-            const int rel = wpos - key0 + nb * 32 + l32;   // the query's position relative to key 0
+            // the query's last visible key, relative to key 0
+            const int rel = CBLK ? qlim[nb] - key0 : wpos - key0 + nb * 32 + l32;
             klim = rel < klim ? (rel < -1 ? -1 : rel) : klim;
           }
         }
@@ -401,8 +420,10 @@ constexpr int kBqKv = RA_KV_BQ;   // queries per LDS tile
 
 // STEP: one backward ring step (ra_blockwise_attn_bwd_step): the queries held are one block at
 // global positions q_pos0 + i, and dK / dV are summed into float32 caller memory (unscaled).
-template <int D, int NKB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC, bool STEP>
+template <int D, int NKB, int CM, bool HAS_BIAS, bool HAS_SEG, int OCC, bool STEP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void dkdv_mfma_kernel(Params p) {
+  constexpr bool CAUSAL = CM != 0;
+  constexpr bool CBLK = CM == 2;
   constexpr int BQ = kBqKv;
   constexpr int KW = 32 * NKB;         // keys per wave
   constexpr int BKW = kWaves * KW;     // keys per workgroup
@@ -571,9 +592,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   };
 
   // query walk with NS - 1 tiles of lookahead: entry 0 is computed, entry NS - 1 is issued
+  // causal limits: positions relative to global kv_pos0 (0 outside a ring step); the walk skips
+  // the query tiles that end before the first query able to see the workgroup's first key
+  const int coff = static_cast<int>(p.kv_pos0);
+  const int64_t qfirst = CBLK ? causal_first_query(static_cast<int>(kfirst), coff, p.causal) : kfirst;
   QueryWalk walk;
-  if constexpr (STEP) walk.begin_step(p.Lq, CAUSAL, kfirst, p.q_pos0 - p.kv_pos0);
-  else walk.begin(p.n_ring, j, p.Lb, CAUSAL, kfirst, p.ring_rank);
+  if constexpr (STEP) walk.begin_step(p.Lq, CAUSAL, qfirst, p.q_pos0 - p.kv_pos0);
+  else walk.begin(p.n_ring, j, p.Lb, CAUSAL, qfirst, p.ring_rank);
   SegTileFilter filt;   // with segment ids: pass over query tiles sharing no id with the keys
   auto next_tile = [&]() -> bool {
     while (walk.next<BQ>()) {
@@ -605,9 +630,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   RA_WAIT_VMCNT(0);
   __syncthreads();
 
-  // 32-bit copies for the per-tile tests (positions are below 2^30, checked on the host)
+  // 32-bit copies for the per-tile tests (positions are below 2^30, checked on the host): the
+  // first query able to see the wave's first and last key, and each lane's key
   const int wkey = static_cast<int>(wkey0);
   const bool wk_ok = wk0 < p.Lb;
+  int wq_first = wkey, wq_last = wkey + KW - 1;
+  int kfq[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) kfq[kb] = wkey + kb * 32 + l32;
+  if constexpr (CBLK) {
+    wq_first = causal_first_query(wkey, coff, p.causal);
+    wq_last = causal_first_query(wkey + KW - 1, coff, p.causal);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) kfq[kb] = causal_first_query(wkey + kb * 32 + l32, coff, p.causal);
+  }
   int slot = 0;
   while (tok[0]) {
     const int row0 = tr0[0], rend = tre[0], pbase = tpb[0];
@@ -622,15 +658,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     const __bf16* Gt = sG[buf];
     const int qpos0 = row0 + pbase;                      // global position of the tile's row 0
     const int nq = (rend - row0) < BQ ? (rend - row0) : BQ;
-    const bool wave_active = wk_ok && !(CAUSAL && qpos0 + nq - 1 < wkey);
+    const bool wave_active = wk_ok && !(CAUSAL && qpos0 + nq - 1 < (CBLK ? wq_first : wkey));
     if (wave_active) {
       // rows past the rank's end carry -inf in sL, so their P is 0 and only the causal and
       // segment masks need the selects
-      const bool need_mask = HAS_SEG || (CAUSAL && wkey + KW - 1 > qpos0);
-      int krel[NKB];   // the lane's key relative to the tile's row 0, clamped to [0, BQ]
+      const bool need_mask = HAS_SEG || (CAUSAL && (CBLK ? wq_last : wkey + KW - 1) > qpos0);
+      int krel[NKB];   // first query row (of the tile) that sees the lane's key, clamped to [0, BQ]
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const int rel = wkey + kb * 32 + l32 - qpos0;
+        const int rel = (CBLK ? kfq[kb] : wkey + kb * 32 + l32) - qpos0;
         krel[kb] = rel < 0 ? 0 : (rel > BQ ? BQ : rel);
       }
 #pragma unroll
@@ -795,13 +831,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 // ================================================================== launchers
 #define RA_SELECT_FLAGS(CALL)                                                      \
   do {                                                                             \
-    const bool c_ = p.causal != 0, b_ = p.bias != nullptr, s_ = p.seg != nullptr;  \
-    if (c_) {                                                                      \
-      if (b_) { if (s_) CALL(true, true, true); else CALL(true, true, false); }    \
-      else { if (s_) CALL(true, false, true); else CALL(true, false, false); }     \
+    const bool b_ = p.bias != nullptr, s_ = p.seg != nullptr;                     \
+    if (p.causal == 1) {                                                           \
+      if (b_) { if (s_) CALL(1, true, true); else CALL(1, true, false); }          \
+      else { if (s_) CALL(1, false, true); else CALL(1, false, false); }           \
+    } else if (p.causal > 1) {                                                     \
+      if (b_) { if (s_) CALL(2, true, true); else CALL(2, true, false); }          \
+      else { if (s_) CALL(2, false, true); else CALL(2, false, false); }           \
     } else {                                                                       \
-      if (b_) { if (s_) CALL(false, true, true); else CALL(false, true, false); }  \
-      else { if (s_) CALL(false, false, true); else CALL(false, false, false); }   \
+      if (b_) { if (s_) CALL(0, true, true); else CALL(0, true, false); }          \
+      else { if (s_) CALL(0, false, true); else CALL(0, false, false); }           \
     }                                                                              \
   } while (0)
 

@@ -41,8 +41,12 @@ struct FwdLds {
 // arithmetic run while the other's matrix products do).
 // STEP: one ring step (see ra_blockwise_attn_fwd_step): the keys held are one block at global
 // positions kv_pos0 + j, the running state is read from and written back to caller memory.
-template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, int OCC, bool STEP>
+// CM: causal mode, 0 none, 1 token level, 2 causal blocks of p.causal > 1 tokens (a mode of its own,
+// so that the common modes compile exactly as they would without block sizes).
+template <int D, int NQB, int CM, bool HAS_BIAS, bool HAS_SEG, int OCC, bool STEP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_mfma_kernel(Params p) {
+  constexpr bool CAUSAL = CM != 0;
+  constexpr bool CBLK = CM == 2;
   constexpr int QW = 32 * NQB;         // queries per wave
   constexpr int BQ = kWaves * QW;      // queries per workgroup
   constexpr int KK = D / 16;           // k-steps of S^T (head_dim / 16)
@@ -222,8 +226,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   };
 
   // ring walk with NS - 1 tiles of lookahead: T[0] is being computed, T[NS-1] is issued
+  // causal limits: relative positions have their origin at global position kv_pos0 (0 outside a
+  // ring step); the walk stops after the last key the workgroup's last query can see
+  const int coff = static_cast<int>(p.kv_pos0);
   RingWalk walk;
-  walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
+  walk.begin(p.n_ring, r, p.Lb, CAUSAL,
+             CBLK && nrows > 0 ? causal_last_key(static_cast<int>(pos0 + nrows - 1), coff, p.causal) : pos0 + nrows - 1);
   // With segment ids the walk passes over tiles that share no id with the workgroup's
   // queries (windows of 64 tiles, see SegTileFilter).
   SegTileFilter filt;
@@ -261,6 +269,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   // are below 2^30, checked on the host), so that per-tile tests stay on the scalar unit
   const int wpos = static_cast<int>(wpos0);
   const int wlast = static_cast<int>(wvalid < QW ? wvalid : QW) - 1;
+  // the last key the wave's first and last query can see, and each lane's own limits
+  int wlim_first = 0, wlim_last = 0;
+  int qlim[NQB];
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) qlim[nb] = 0;
+  if constexpr (CBLK) {
+    wlim_first = causal_last_key(wpos, coff, p.causal);
+    wlim_last = wlast >= 0 ? causal_last_key(wpos + wlast, coff, p.causal) : -1;
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) qlim[nb] = causal_last_key(wpos + nb * 32 + l32, coff, p.causal);
+  }
   int slot = 0;
   while (tok[0]) {
     const int key0 = tk0[0], kend = tke[0];
@@ -273,7 +292,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     const int buf = slot;
     const __bf16* Kt = sK[buf];
     const __bf16* Vt = sV[buf];
-    bool wave_active = wlast >= 0 && !(CAUSAL && key0 > wpos + wlast);
+    bool wave_active = wlast >= 0 && !(CAUSAL && key0 > (CBLK ? wlim_last : wpos + wlast));
     if constexpr (HAS_SEG) {
       // no key of the tile shares a segment with the wave's queries: every pair is masked
       const int klo = __builtin_amdgcn_readfirstlane(sSegRange[buf][0]);
@@ -298,7 +317,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         }
       }
 
-      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > wpos);
+      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > (CBLK ? wlim_first : wpos));
       int kseg[2][16];
       if constexpr (HAS_SEG) {
 #pragma unroll
@@ -330,7 +349,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
           // segments, its id equals the query's; applied with selects, no branches
           int klim = (kend - key0 < BK ? kend - key0 : BK) - 1;
           if constexpr (CAUSAL) {
-            const int rel = wpos - key0 + nb * 32 + l32;   // the query's position relative to key 0
+            // the query's last visible key, relative to key 0
+            const int rel = CBLK ? qlim[nb] - key0 : wpos - key0 + nb * 32 + l32;
             klim = rel < klim ? (rel < -1 ? -1 : rel) : klim;
           }
 #pragma unroll
@@ -467,7 +487,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   }
 }
 
-template <int D, int NQB, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG, bool STEP>
+template <int D, int NQB, int CM, bool HAS_BIAS, bool HAS_SEG, bool STEP>
 hipError_t launch_t(const Params& p, hipStream_t st) {
   constexpr int BQ = kWaves * 32 * NQB;
   const int64_t n_qt = (p.ring_rank < 0 ? p.n_ring : 1) * ((p.Lb + BQ - 1) / BQ);
@@ -476,20 +496,23 @@ hipError_t launch_t(const Params& p, hipStream_t st) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   // segment ids cost registers: those variants keep one wave per SIMD rather than spill
   constexpr int OCC = (HAS_SEG || (HAS_BIAS && D == 64)) ? 1 : 2;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, NQB, CAUSAL, HAS_BIAS, HAS_SEG, OCC, STEP>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, NQB, CM, HAS_BIAS, HAS_SEG, OCC, STEP>), dim3(static_cast<unsigned>(grid)),
                      dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
+template <int D, int NQB, int CM, bool STEP>
+hipError_t launch_m(const Params& p, hipStream_t st) {
+  const bool bi = p.bias != nullptr, sg = p.seg != nullptr;
+  if (bi) return sg ? launch_t<D, NQB, CM, true, true, STEP>(p, st) : launch_t<D, NQB, CM, true, false, STEP>(p, st);
+  return sg ? launch_t<D, NQB, CM, false, true, STEP>(p, st) : launch_t<D, NQB, CM, false, false, STEP>(p, st);
+}
+
 template <int D, int NQB, bool STEP>
 hipError_t launch_d(const Params& p, hipStream_t st) {
-  const bool c = p.causal != 0, bi = p.bias != nullptr, sg = p.seg != nullptr;
-  if (c) {
-    if (bi) return sg ? launch_t<D, NQB, true, true, true, STEP>(p, st) : launch_t<D, NQB, true, true, false, STEP>(p, st);
-    return sg ? launch_t<D, NQB, true, false, true, STEP>(p, st) : launch_t<D, NQB, true, false, false, STEP>(p, st);
-  }
-  if (bi) return sg ? launch_t<D, NQB, false, true, true, STEP>(p, st) : launch_t<D, NQB, false, true, false, STEP>(p, st);
-  return sg ? launch_t<D, NQB, false, false, true, STEP>(p, st) : launch_t<D, NQB, false, false, false, STEP>(p, st);
+  if (p.causal == 0) return launch_m<D, NQB, 0, STEP>(p, st);
+  if (p.causal == 1) return launch_m<D, NQB, 1, STEP>(p, st);
+  return launch_m<D, NQB, 2, STEP>(p, st);
 }
 
 }  // namespace

@@ -107,7 +107,11 @@ int check_shape(const ra_shape* s, int32_t n_ring, Checked* c) {
 int check_mask_args(const ra_shape* s, const float* bias, int64_t q_chunk, int64_t k_chunk, int32_t causal,
                     Checked* c) {
   const int64_t Lb = c->p.Lb;
-  if (causal != 0 && causal != 1) return fail(RA_ERR_ARG, "causal must be 0 or 1 (got %d)", causal);
+  // causal = 0: no mask; causal = c >= 1: causal block size (1: token-level causal attention)
+  if (causal < 0 || causal >= kMaxPos)
+    return fail(RA_ERR_ARG, "causal must be 0 or a causal block size in [1, 2^30) (got %d)", causal);
+  if (causal > 1 && Lb > 0 && Lb % causal != 0)
+    return fail(RA_ERR_ARG, "causal block size %d must divide the ring block length %lld", causal, (long long)Lb);
   if (q_chunk < 1 || k_chunk < 1) return fail(RA_ERR_ARG, "q_chunk and k_chunk must be >= 1");
   if (Lb > 0 && (Lb % q_chunk != 0 || Lb % k_chunk != 0))
     return fail(RA_ERR_ARG, "q_chunk %lld and k_chunk %lld must divide the ring block length %lld",

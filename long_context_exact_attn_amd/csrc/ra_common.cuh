@@ -42,7 +42,8 @@ struct Params {
   void* dk;
   void* dv;
   int64_t Lq, Lk, Lb, bias_len;
-  int32_t B, H, D, n_ring, ring_rank, causal;
+  int32_t B, H, D, n_ring, ring_rank;
+  int32_t causal;           // causal block size (1: token-level causal), 0: no causal mask
   int32_t bf16;             // 1: bfloat16 tensors, 0: float32
   float scale;              // resolved (> 0)
   // one ring step (ra_blockwise_attn_fwd_step): the keys held are global positions
@@ -69,6 +70,24 @@ template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return
 
 __device__ __forceinline__ int64_t row_offset(int b, int64_t row, int h, int64_t L, int H, int D) {
   return ((static_cast<int64_t>(b) * L + row) * H + h) * static_cast<int64_t>(D);
+}
+
+// ---------------------------------------------------------------- causal block size
+// With causal block size c (c = 1: token-level causal attention), positions fall into blocks
+// of c tokens and a key is visible to a query when the key's block does not come after the
+// query's.  Positions here are relative to an origin at global position off >= 0 (so that
+// rel + off >= 0 is the global position).
+// The last key position a query at rel can see: the end of its block.
+__device__ __forceinline__ int causal_last_key(int rel, int off, int c) {
+  if (c == 1) return rel;
+  const int g = rel + off;
+  return (g / c + 1) * c - 1 - off;
+}
+// The first query position that can see a key at rel: the start of the key's block.
+__device__ __forceinline__ int causal_first_query(int rel, int off, int c) {
+  if (c == 1) return rel;
+  const int g = rel + off;
+  return (g / c) * c - off;
 }
 
 // ---------------------------------------------------------------- forward-direction ring walk

@@ -53,7 +53,9 @@ __global__ __launch_bounds__(kLanes) void fwd_simt_kernel(Params p) {
   float m = -INFINITY, l = 0.f;
 
   RingWalk walk;
-  walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
+  walk.begin(p.n_ring, r, p.Lb, CAUSAL,
+             CAUSAL && nrows > 0 ? causal_last_key(static_cast<int>(pos0 + nrows - 1), 0, p.causal) : pos0 + nrows - 1);
+  const int64_t qlim = CAUSAL ? causal_last_key(static_cast<int>(qpos), 0, p.causal) : qpos;   // last visible key
   while (nrows > 0 && walk.next<BKS>()) {
     const int64_t key0 = walk.key0, kend = walk.kend;
     __syncthreads();
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(kLanes) void fwd_simt_kernel(Params p) {
     for (int j = 0; j < BKS; ++j) {
       const int64_t key = key0 + j;
       bool vis = key < kend;
-      if (CAUSAL) vis = vis && key <= qpos;
+      if (CAUSAL) vis = vis && key <= qlim;
       if (HAS_SEG) vis = vis && sS[j] == qseg;
       float acc = 0.f;
       for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qr[d], sK[j][d], acc);
@@ -231,7 +233,10 @@ __global__ __launch_bounds__(kLanes) void dkdv_simt_kernel(Params p) {
   const float c = p.scale * kLog2e;
 
   QueryWalk walk;
-  walk.begin(p.n_ring, j, p.Lb, CAUSAL, kfirst, p.ring_rank);
+  // the first query able to see this thread's key, and the first able to see the tile's first key
+  const int64_t kfq = CAUSAL ? causal_first_query(static_cast<int>(key), 0, p.causal) : key;
+  walk.begin(p.n_ring, j, p.Lb, CAUSAL, CAUSAL ? causal_first_query(static_cast<int>(kfirst), 0, p.causal) : kfirst,
+             p.ring_rank);
   while (walk.next<BQS>()) {
     const int64_t row0 = walk.row0, rend = walk.rend, pbase = walk.pos_base;
     __syncthreads();
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(kLanes) void dkdv_simt_kernel(Params p) {
     for (int i = 0; i < BQS; ++i) {
       const int64_t qpos = sP[i];
       bool vis = qpos >= 0;
-      if (CAUSAL) vis = vis && key <= qpos;
+      if (CAUSAL) vis = vis && qpos >= kfq;
       if (HAS_SEG) vis = vis && sS[i] == kseg;
       if (!vis) continue;
       float s = 0.f, dp = 0.f;
@@ -324,7 +329,9 @@ __global__ __launch_bounds__(kLanes) void dq_simt_kernel(Params p) {
   const float c = p.scale * kLog2e;
 
   RingWalk walk;
-  walk.begin(p.n_ring, r, p.Lb, CAUSAL, pos0 + nrows - 1);
+  walk.begin(p.n_ring, r, p.Lb, CAUSAL,
+             CAUSAL && nrows > 0 ? causal_last_key(static_cast<int>(pos0 + nrows - 1), 0, p.causal) : pos0 + nrows - 1);
+  const int64_t qlim = CAUSAL ? causal_last_key(static_cast<int>(qpos), 0, p.causal) : qpos;   // last visible key
   while (nrows > 0 && walk.next<BKS>()) {
     const int64_t key0 = walk.key0, kend = walk.kend;
     __syncthreads();
@@ -346,7 +353,7 @@ __global__ __launch_bounds__(kLanes) void dq_simt_kernel(Params p) {
     for (int j = 0; j < BKS; ++j) {
       const int64_t key = key0 + j;
       bool vis = key < kend;
-      if (CAUSAL) vis = vis && key <= qpos;
+      if (CAUSAL) vis = vis && key <= qlim;
       if (HAS_SEG) vis = vis && sS[j] == qseg;
       if (!vis) continue;
       float s = 0.f, dp = 0.f;

@@ -15,34 +15,24 @@ import numpy as np
 def visible_pairs_per_head(q_first, q_len, kv_len, causal, segment_ids=None):
     """Visible pairs of one head, summed over the batch rows of segment_ids (or one row).
 
-    Queries sit at global positions q_first .. q_first + q_len - 1.
+    Queries sit at global positions q_first .. q_first + q_len - 1.  causal is False / 0 (no
+    mask), True (token level) or a causal block size c: a query at p sees keys below
+    min((p // c + 1) * c, kv_len).
     """
     if q_len <= 0 or kv_len <= 0:
         return 0
+    c = 0 if causal is None or causal is False else (1 if causal is True else int(causal))
+    qpos = np.arange(q_first, q_first + q_len, dtype=np.int64)
+    lim = np.minimum((qpos // c + 1) * c, kv_len) if c else np.full(q_len, kv_len, dtype=np.int64)
     if segment_ids is None:
-        if not causal:
-            return q_len * kv_len
-        lo, hi = q_first + 1, q_first + q_len          # sum of (p + 1) over the query positions
-        return (lo + hi) * q_len // 2
+        return int(lim.sum())
     total = 0
-    seg = np.asarray(segment_ids)
-    for row in seg:
+    for row in np.asarray(segment_ids):
         row = row.astype(np.int64)
-        qpos = np.arange(q_first, q_first + q_len)
-        if causal:
-            # 1 + the number of earlier keys with the same id: rank inside the id's run
-            order = np.argsort(row, kind="stable")
-            sorted_ids = row[order]
-            starts = np.zeros(len(row), dtype=np.int64)
-            bounds = np.flatnonzero(np.diff(sorted_ids)) + 1
-            starts[bounds] = bounds
-            starts = np.maximum.accumulate(starts)
-            rank = np.empty(len(row), dtype=np.int64)
-            rank[order] = np.arange(len(row)) - starts
-            total += int((rank[qpos] + 1).sum())
-        else:
-            inv = np.unique(row, return_inverse=True)[1]
-            total += int(np.bincount(inv)[inv][qpos].sum())
+        # keys of the query's segment below its limit: sort (id, position) pairs and count
+        comb = np.sort((row - row.min()) * (kv_len + 1) + np.arange(kv_len, dtype=np.int64))
+        base = (row[qpos] - row.min()) * (kv_len + 1)
+        total += int((np.searchsorted(comb, base + lim) - np.searchsorted(comb, base)).sum())
     return total
 
 

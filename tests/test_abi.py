@@ -71,7 +71,7 @@ def _fwd(lib, shape, n_ring=4, q_chunk=64, k_chunk=64, causal=1, out=None, lse=N
 @needs_cpu
 @pytest.mark.parametrize("case,expect", [
     ("ring_not_closed", -2), ("rank_out_of_range", -1), ("q_len_vs_rank", -2), ("all_ranks_q_len", -2),
-    ("head_dim", -3), ("dtype", -3), ("negative", -2), ("causal", -1), ("chunk_zero", -1),
+    ("head_dim", -3), ("dtype", -3), ("negative", -2), ("causal", -1), ("causal_negative", -1), ("chunk_zero", -1),
     ("chunk_not_dividing", -1), ("n_ring_zero", -1), ("bias_len", -1), ("null_out", -1), ("null_lse", -1),
     ("null_q", -1), ("misaligned_k", -1), ("null_shape", -1),
 ])
@@ -96,7 +96,9 @@ def test_forward_validation(case, expect):
     elif case == "negative":
         shape = S(batch=-1)
     elif case == "causal":
-        kw["causal"] = 2
+        kw["causal"] = 3   # a causal block size that does not divide the ring block of 256
+    elif case == "causal_negative":
+        kw["causal"] = -1
     elif case == "chunk_zero":
         kw["q_chunk"] = 0
     elif case == "chunk_not_dividing":

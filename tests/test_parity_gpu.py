@@ -119,6 +119,15 @@ SWEEP = [
     ("docs-long", dict(kv_len=12288, n_ring=3, ring_rank=2, segments="docs", doc_len=(50, 3000), heads=2)),
     ("docs-long-d128", dict(head_dim=128, kv_len=9216, n_ring=2, segments="docs", doc_len=(20, 5000), heads=2,
                             bias_len=512)),
+    # causal block sizes c > 1 (a key is visible when its block of c tokens does not come after the
+    # query's): c below, equal to and above the 64-token tile, a ragged block, with masks and bias
+    ("causal-block-64", dict(kv_len=1024, n_ring=4, causal=64)),
+    ("causal-block-16-ragged", dict(kv_len=1000, n_ring=4, causal=50)),
+    ("causal-block-128-rank2", dict(kv_len=2048, n_ring=4, ring_rank=2, causal=128, segments="docs", doc_len=(30, 500),
+                                    bias_len=100)),
+    ("causal-block-whole-ring-block", dict(kv_len=1024, n_ring=4, causal=256)),
+    ("causal-block-d128", dict(head_dim=128, kv_len=1536, n_ring=3, causal=256, heads=3)),
+    ("causal-block-f32", dict(dtype="f32", kv_len=512, n_ring=2, causal=32, bias_len=9)),
     # unsorted ids, int32 extremes included: tile skipping must stay exact for any ids
     ("ids-scattered", dict(kv_len=6144, n_ring=3, segments="scattered", heads=2)),
     ("ids-scattered-noncausal", dict(kv_len=2048, n_ring=2, causal=False, segments="scattered", bias_len=77)),

@@ -46,6 +46,8 @@ CASES = [
     ("seg-noncausal", dict(kv_len=1536, n_ring=3, ring_rank=2, causal=False, segments="docs", doc_len=(5, 120))),
     ("d128-batch2", dict(head_dim=128, batch=2, heads=3, kv_len=1024, n_ring=2, ring_rank=1, bias_len=77)),
     ("heads5-ring8", dict(heads=5, kv_len=2048, n_ring=8, ring_rank=5)),
+    ("causal-block-64-r2", dict(kv_len=2048, n_ring=4, ring_rank=2, causal=64, segments="docs", doc_len=(40, 300))),
+    ("causal-block-100-r1", dict(kv_len=1200, n_ring=3, ring_rank=1, causal=100, bias_len=30)),
 ]
 
 
@@ -185,6 +187,8 @@ BWD_CASES = [
     ("noncausal-bias-seg", dict(kv_len=1536, n_ring=3, causal=False, bias_len=100, segments="docs", doc_len=(20, 400))),
     ("ragged-250", dict(kv_len=1000, n_ring=4, segments="scattered")),
     ("d128-batch2", dict(head_dim=128, batch=2, heads=3, kv_len=1024, n_ring=2, bias_len=64)),
+    ("causal-block-32", dict(kv_len=1024, n_ring=4, causal=32, segments="docs", doc_len=(20, 200))),
+    ("causal-block-100", dict(kv_len=1200, n_ring=3, causal=100)),
 ]
 
 
