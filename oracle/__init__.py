@@ -21,7 +21,7 @@ Modules
 -------
 ``attention``  the plain definition, softmax(scale*QK^T + bias + mask) V, and
                its gradients, in float64 (``forward``, ``backward``,
-               ``probabilities``).
+               ``bias_grad``, ``probabilities``).
 ``blockwise``  the method's own procedure -- ring-order steps over K/V
                blocks, query/key chunks, online-softmax merge -- in float64,
                used to pin the claim that the procedure is exact.
@@ -30,5 +30,6 @@ Parity status: every function here is pinned by CPU tests (brute force,
 library special case, closed forms, finite differences, invariants); none is
 "parity unpinned".
 """
-from .attention import forward, backward, probabilities, query_positions, visible_pairs, causal_block  # noqa: F401
+from .attention import (forward, backward, bias_grad, probabilities, query_positions, visible_pairs,  # noqa: F401
+                        causal_block)
 from .blockwise import ring_forward  # noqa: F401

@@ -201,6 +201,37 @@ def backward(q, k, v, dout, *, q_pos, causal, scale=None, bias=None, segment_ids
     return dq, dk, dv, delta
 
 
+def bias_grad(q, k, v, dout, *, q_pos, causal, scale=None, bias, segment_ids=None):
+    """Gradient of sum(dout * out) w.r.t. the additive bias [H, bias_len], in float64.
+
+    Key j adds bias[h, j mod bias_len] to every query's score, so the bias entry t collects
+    dS_ij = dL/ds_ij over all batch rows, queries i and keys j with j mod bias_len = t (the bias
+    is not scaled).  P is recomputed as in ``backward``.  Returns dbias [H, bias_len].
+    """
+    B, nq, H, D = q.shape
+    Lk = k.shape[1]
+    scale = _default_scale(scale, D)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    bias = np.asarray(bias, dtype=np.float64)
+    nb = bias.shape[1]
+    dbias = np.zeros((H, nb), dtype=np.float64)
+    for b in range(B):
+        seg_row = None if segment_ids is None else np.asarray(segment_ids[b])
+        for h in range(H):
+            kb = np.asarray(k[b, :, h, :], dtype=np.float64)
+            vb = np.asarray(v[b, :, h, :], dtype=np.float64)
+            brow = _bias_row(bias, h, Lk)
+            for i0, i1 in _chunks(nq, Lk):
+                qb = np.asarray(q[b, i0:i1, h, :], dtype=np.float64)
+                dob = np.asarray(dout[b, i0:i1, h, :], dtype=np.float64)
+                vis = _visible(q_pos[i0:i1], Lk, causal, seg_row)
+                p, _ = _softmax_rows(_scores(qb, kb, scale, brow, vis))
+                dl = np.sum(dob * (p @ vb), axis=1)
+                ds = p * (dob @ vb.T - dl[:, None])
+                np.add.at(dbias[h], np.arange(Lk) % nb, ds.sum(axis=0))
+    return dbias
+
+
 def visible_pairs(q_pos, kv_len, causal, segment_ids=None):
     """Number of visible (query, key) pairs per head, summed over the batch.
 

@@ -395,3 +395,48 @@ def test_ring_forward_causal_blocks():
         ro, rl = oracle.forward(q, k, v, q_pos=pos, causal=c, bias=bias, segment_ids=segs)
         np.testing.assert_allclose(o, ro, atol=1e-12)
         np.testing.assert_allclose(l_, rl, atol=1e-12)
+
+
+# ---------------------------------------------------------------- bias gradient
+@pytest.mark.parametrize("causal,seg,bias_len", [(False, False, 7), (True, True, 5), (3, False, 24), (True, False, 50)])
+def test_bias_grad_against_torch_autograd(causal, seg, bias_len):
+    # library special case: SDPA with the bias gathered by key position as a leaf tensor
+    q, k, v, bias, segs, pos = _rand_case(B=2, L=24, H=3, D=8, n_ring=4, ring_rank=-1, bias_len=bias_len, seg=seg,
+                                           seed=31)
+    if segs is not None:
+        segs = np.sort(segs, axis=1)
+    scale = 0.41
+    B, L, H, D = q.shape
+    tb = torch.tensor(bias, requires_grad=True)
+    tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3).copy()) for x in (q, k, v))
+    j, p = torch.arange(L), torch.as_tensor(pos)
+    add = tb[:, j % bias_len][None, :, None, :].expand(B, H, L, L)
+    c = oracle.causal_block(causal)
+    mask = torch.zeros((B, H, L, L), dtype=torch.bool)
+    if c:
+        mask |= ((j // c)[None, :] > (p // c)[:, None])[None, None]
+    if segs is not None:
+        st = torch.as_tensor(segs)
+        mask |= (st[:, None, :] != st[:, p][:, :, None])[:, None]
+    add = add.masked_fill(mask, float("-inf"))
+    t_out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=add, scale=scale)
+    dout = np.random.default_rng(32).standard_normal(q.shape)
+    t_out.backward(torch.tensor(dout.transpose(0, 2, 1, 3).copy()))
+    mine = oracle.bias_grad(q, k, v, dout, q_pos=pos, causal=causal, scale=scale, bias=bias, segment_ids=segs)
+    np.testing.assert_allclose(mine, tb.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_bias_grad_sums_to_zero_and_matches_finite_differences():
+    q, k, v, bias, segs, pos = _rand_case(B=1, L=12, H=2, D=4, n_ring=3, ring_rank=1, bias_len=5, seg=True, seed=33)
+    dout = np.random.default_rng(34).standard_normal(q.shape)
+    g = oracle.bias_grad(q, k, v, dout, q_pos=pos, causal=True, bias=bias, segment_ids=segs)
+    # every row of P sums to 1, so the scores' gradient sums to 0 over each row's keys
+    np.testing.assert_allclose(g.sum(axis=1), 0.0, atol=1e-13)
+    eps = 1e-6
+    for h, t in ((0, 0), (1, 3), (1, 4)):
+        bp, bm = bias.copy(), bias.copy()
+        bp[h, t] += eps
+        bm[h, t] -= eps
+        fp = np.sum(dout * oracle.forward(q, k, v, q_pos=pos, causal=True, bias=bp, segment_ids=segs)[0])
+        fm = np.sum(dout * oracle.forward(q, k, v, q_pos=pos, causal=True, bias=bm, segment_ids=segs)[0])
+        assert abs((fp - fm) / (2 * eps) - g[h, t]) < 1e-7

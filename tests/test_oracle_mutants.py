@@ -43,6 +43,11 @@ MUTANTS = {
     "dq_unscaled": ("dq[b, i0:i1, h, :] = scale * (ds @ kb)", "dq[b, i0:i1, h, :] = ds @ kb"),
     "dq_uses_values": ("dq[b, i0:i1, h, :] = scale * (ds @ kb)", "dq[b, i0:i1, h, :] = scale * (ds @ vb)"),
     "dp_uses_keys": ("dp = dob @ vb.T", "dp = dob @ kb.T"),
+    "dbias_is_p": ("ds = p * (dob @ vb.T - dl[:, None])", "ds = p"),
+    "dbias_wrong_index": ("np.add.at(dbias[h], np.arange(Lk) % nb, ds.sum(axis=0))",
+                          "np.add.at(dbias[h], (np.arange(Lk) // nb) % nb, ds.sum(axis=0))"),
+    "dbias_scaled": ("np.add.at(dbias[h], np.arange(Lk) % nb, ds.sum(axis=0))",
+                     "np.add.at(dbias[h], np.arange(Lk) % nb, scale * ds.sum(axis=0))"),
 }
 
 
@@ -141,7 +146,29 @@ def pin_causal_blocks(M):
     assert M.visible_pairs(np.arange(L), L, c) == sum((p // c + 1) * c for p in range(L))
 
 
-PINS = [pin_worked_examples, pin_zero_keys_per_rank, pin_sdpa, pin_gradient_invariants, pin_causal_blocks]
+def pin_bias_grad(M):
+    # torch autograd through the bias gathered by key position (library special case), and the
+    # gradient of the scores summing to zero over each query's keys
+    q, k, v, bias, segs, pos = _case(9, bias_len=5)
+    scale = 0.45
+    B, Lq, H, D = q.shape
+    Lk = k.shape[1]
+    tb = torch.tensor(bias, requires_grad=True)
+    tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3).copy()) for x in (q, k, v))
+    j, p = torch.arange(Lk), torch.as_tensor(pos)
+    st = torch.as_tensor(segs)
+    mask = (j[None, :] > p[:, None])[None, None] | (st[:, None, :] != st[:, p][:, :, None])[:, None]
+    add = tb[:, j % bias.shape[1]][None, :, None, :].expand(B, H, Lq, Lk).masked_fill(mask, float("-inf"))
+    t_out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=add, scale=scale)
+    dout = np.random.default_rng(10).standard_normal(q.shape)
+    t_out.backward(torch.tensor(dout.transpose(0, 2, 1, 3).copy()))
+    g = M.bias_grad(q, k, v, dout, q_pos=pos, causal=True, scale=scale, bias=bias, segment_ids=segs)
+    np.testing.assert_allclose(g, tb.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(g.sum(axis=1), 0.0, atol=1e-12)
+
+
+PINS = [pin_worked_examples, pin_zero_keys_per_rank, pin_sdpa, pin_gradient_invariants, pin_causal_blocks,
+        pin_bias_grad]
 
 
 def test_pins_pass_on_the_oracle():
