@@ -111,6 +111,25 @@ int ra_blockwise_attn_fwd(const void* q, const void* k, const void* v, const flo
 size_t ra_blockwise_attn_bwd_workspace_size(const ra_shape* shape);
 
 /*
+ * The backward pass plus the gradient of the additive bias (NEXT-4 of the pages' attention_bias,
+ * "RingAttention核心功能全解析", 快速上手; the pages define no gradient, the plain one is taken):
+ * key j adds bias[h, j mod bias_len] to every query's score, so
+ *   dbias[h, t] = sum over b, i and keys j with j mod bias_len = t of dS_ij   (float32, [H, bias_len])
+ * with dS as above (no scale factor).  Arguments as ra_blockwise_attn_bwd, plus dbias (device,
+ * 4-byte aligned); bias must be given and the dtype must be RA_BF16.  The workspace must hold
+ * ra_blockwise_attn_bwd_dbias_workspace_size(shape) bytes (Delta and per-key sums of dS).  The
+ * sums run in a fixed order: the result is deterministic.
+ */
+int ra_blockwise_attn_bwd_dbias(const void* q, const void* k, const void* v, const float* bias,
+                                const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                                int32_t causal, const void* out, const float* lse, const void* dout, void* dq,
+                                void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes,
+                                const ra_shape* shape, void* stream);
+
+/* Workspace bytes ra_blockwise_attn_bwd_dbias needs for this shape. */
+size_t ra_blockwise_attn_bwd_dbias_workspace_size(const ra_shape* shape);
+
+/*
  * Backward pass: recomputes P from lse and writes dq, dk, dv (dtype, same
  * layouts as q, k, v, written in full).  out and lse are the forward's
  * outputs for the same arguments.  Runs the three phases below in order on

@@ -59,13 +59,15 @@ def load_library():
         "ra_attn_merge": [P, P, P, P, SH, P],
         "ra_blockwise_attn_bwd_step": [P, P, P, P, P, I64, I64, I64, I32, P, P, P, P, P, P, I32, I32, SH, P],
         "ra_blockwise_attn_bwd_finalize": [P, P, P, P, P, P, SH, P],
+        "ra_blockwise_attn_bwd_dbias": [P, P, P, P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, P, SZ, SH, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
-    lib.ra_blockwise_attn_bwd_workspace_size.argtypes = [SH]
-    lib.ra_blockwise_attn_bwd_workspace_size.restype = SZ
+    for name in ("ra_blockwise_attn_bwd_workspace_size", "ra_blockwise_attn_bwd_dbias_workspace_size"):
+        getattr(lib, name).argtypes = [SH]
+        getattr(lib, name).restype = SZ
     lib.ra_last_error.argtypes = []
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_abi_version.argtypes = []
@@ -168,6 +170,31 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, bias=None, segment_ids=None, *, 
                                      workspace.numel() * workspace.element_size(), ctypes.byref(shape),
                                      _stream(q.device)))
     return dq, dk, dv
+
+
+def blockwise_attn_bwd_dbias(q, k, v, out, lse, dout, bias, segment_ids=None, *, n_ring, q_chunk, k_chunk, causal,
+                             ring_rank=-1, scale=None, dq=None, dk=None, dv=None, dbias=None, workspace=None):
+    """dq, dk, dv, dbias = ra_blockwise_attn_bwd_dbias(...): the backward plus the bias gradient
+    (float32 [heads, bias_len])."""
+    lib = load_library()
+    _tensors(q, k, v, bias, segment_ids, extra=(("out", out), ("lse", lse), ("dout", dout)))
+    if bias is None:
+        raise ValueError("the bias gradient needs a bias")
+    shape = make_shape(q, k, ring_rank=ring_rank, scale=scale, bias=bias)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dbias = torch.empty_like(bias) if dbias is None else dbias
+    _tensors(q, k, v, None, None, extra=(("dbias", dbias),))
+    need = int(lib.ra_blockwise_attn_bwd_dbias_workspace_size(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.ra_blockwise_attn_bwd_dbias(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(n_ring),
+                                           int(q_chunk), int(k_chunk), _causal(causal), _ptr(out), _ptr(lse),
+                                           _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), ctypes.byref(shape),
+                                           _stream(q.device)))
+    return dq, dk, dv, dbias
 
 
 def blockwise_attn_bwd_preprocess(out, dout, *, delta=None):

@@ -507,6 +507,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   }
 
   const float c = p.scale * kLog2e;
+  // with a bias (outside ring steps): the lane's part of sum_i dS_ij for its key, the bias gradient
+  constexpr bool KEYSUM = HAS_BIAS && !STEP;
+  float dsum[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) dsum[kb] = 0.f;
   f32x16 dK[DB][NKB], dV[DB][NKB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -738,6 +743,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
             }
             Pb[kb][st] = pack_bf16x8(pe);
             Sb[kb][st] = pack_bf16x8(de);
+            if constexpr (KEYSUM) dsum[kb] += ((de[0] + de[1]) + (de[2] + de[3])) + ((de[4] + de[5]) + (de[6] + de[7]));
           }
         // dV^T += dO^T . P ;  dK^T += Q^T . dS
 #pragma unroll
@@ -804,6 +810,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         }
     }
     return;
+  }
+  if constexpr (KEYSUM) {
+    if (p.dbias_keys) {
+      // lanes l and l + 32 hold the same key for different queries
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float t = pair_sum(dsum[kb]);
+        const int64_t krow = wk0 + kb * 32 + l32;
+        if (hh == 0 && krow < p.Lb)
+          p.dbias_keys[(static_cast<int64_t>(b) * p.H + h) * p.Lk + static_cast<int64_t>(j) * p.Lb + krow] = t;
+      }
+    }
   }
   __bf16* __restrict__ dkp = static_cast<__bf16*>(p.dk);
   __bf16* __restrict__ dvp = static_cast<__bf16*>(p.dv);

@@ -197,6 +197,12 @@ size_t ra_blockwise_attn_bwd_workspace_size(const ra_shape* shape) {
   return (rows * sizeof(float) + 255) / 256 * 256;
 }
 
+size_t ra_blockwise_attn_bwd_dbias_workspace_size(const ra_shape* shape) {
+  if (!shape || shape->batch < 0 || shape->heads < 0 || shape->q_len < 0 || shape->kv_len < 0) return 0;
+  return ra_blockwise_attn_bwd_workspace_size(shape) +
+         static_cast<size_t>(shape->batch) * shape->heads * shape->kv_len * sizeof(float);
+}
+
 int ra_blockwise_attn_bwd_preprocess(const void* out, const void* dout, float* delta, const ra_shape* shape,
                                      void* stream) {
   RA_TRY(check_dims(shape));
@@ -268,18 +274,26 @@ int ra_blockwise_attn_bwd_dq(const void* q, const void* k, const void* v, const 
   return do_bwd_dq(c, static_cast<hipStream_t>(stream));
 }
 
-int ra_blockwise_attn_bwd(const void* q, const void* k, const void* v, const float* bias,
-                          const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
-                          int32_t causal, const void* out, const float* lse, const void* dout, void* dq,
-                          void* dk, void* dv, void* workspace, size_t workspace_bytes_given,
-                          const ra_shape* shape, void* stream) {
+// The whole backward: Delta into the workspace, then dK/dV, then dQ; with dbias, the dK/dV kernel
+// also leaves per-key sums of dS in the workspace, reduced into dbias afterwards.
+static int bwd_full(const void* q, const void* k, const void* v, const float* bias, const int32_t* segment_ids,
+                    int32_t n_ring, int64_t q_chunk, int64_t k_chunk, int32_t causal, const void* out,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dbias, void* workspace,
+                    size_t workspace_bytes_given, const ra_shape* shape, void* stream) {
   Checked c;
   RA_TRY(bwd_common(q, k, v, bias, segment_ids, n_ring, q_chunk, k_chunk, causal, lse, dout, shape, &c));
   RA_TRY(need_ptr(out, c.q_elems, "out", 16));
   RA_TRY(need_ptr(dq, c.q_elems, "dq", 16));
   RA_TRY(need_ptr(dk, c.kv_elems, "dk", 16));
   RA_TRY(need_ptr(dv, c.kv_elems, "dv", 16));
-  const size_t need = workspace_bytes(c);
+  const size_t delta_bytes = workspace_bytes(c);
+  size_t need = delta_bytes;
+  if (dbias) {
+    if (!bias) return fail(RA_ERR_ARG, "dbias needs a bias");
+    if (shape->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "dbias is implemented for RA_BF16 only");
+    RA_TRY(need_ptr(dbias, static_cast<int64_t>(shape->heads) * shape->bias_len, "dbias", 4));
+    need += static_cast<size_t>(shape->batch) * shape->heads * shape->kv_len * sizeof(float);
+  }
   if (need > 0 && (!workspace || workspace_bytes_given < need))
     return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes_given,
                 workspace ? "" : " (NULL)");
@@ -292,10 +306,40 @@ int ra_blockwise_attn_bwd(const void* q, const void* k, const void* v, const flo
   c.p.dq = dq;
   c.p.dk = dk;
   c.p.dv = dv;
+  c.p.dbias_keys = dbias ? reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes) : nullptr;
   if (c.rows > 0) RA_TRY(hip_status(ra::launch_bwd_preprocess(c.p, st), "preprocess launch"));
   if (c.kv_elems > 0) RA_TRY(do_bwd_dkdv(c, st));
   if (c.rows > 0) RA_TRY(do_bwd_dq(c, st));
+  if (dbias) {
+    if (c.kv_elems == 0 || c.rows == 0) {
+      // nothing visible: dbias is zero (the key sums were not written)
+      RA_TRY(hip_status(hipMemsetAsync(dbias, 0, sizeof(float) * shape->heads * shape->bias_len, st), "dbias clear"));
+    } else {
+      RA_TRY(hip_status(ra::launch_bias_grad(c.p.dbias_keys, dbias, shape->batch, shape->heads, shape->kv_len,
+                                             shape->bias_len, st),
+                        "dbias launch"));
+    }
+  }
   return ok();
+}
+
+int ra_blockwise_attn_bwd(const void* q, const void* k, const void* v, const float* bias,
+                          const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                          int32_t causal, const void* out, const float* lse, const void* dout, void* dq,
+                          void* dk, void* dv, void* workspace, size_t workspace_bytes_given,
+                          const ra_shape* shape, void* stream) {
+  return bwd_full(q, k, v, bias, segment_ids, n_ring, q_chunk, k_chunk, causal, out, lse, dout, dq, dk, dv, nullptr,
+                  workspace, workspace_bytes_given, shape, stream);
+}
+
+int ra_blockwise_attn_bwd_dbias(const void* q, const void* k, const void* v, const float* bias,
+                                const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                                int32_t causal, const void* out, const float* lse, const void* dout, void* dq,
+                                void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes_given,
+                                const ra_shape* shape, void* stream) {
+  if (!dbias) return fail(RA_ERR_ARG, "dbias is NULL");
+  return bwd_full(q, k, v, bias, segment_ids, n_ring, q_chunk, k_chunk, causal, out, lse, dout, dq, dk, dv, dbias,
+                  workspace, workspace_bytes_given, shape, stream);
 }
 
 int ra_blockwise_attn_fwd_step(const void* q, const void* k, const void* v, const float* bias,

@@ -59,6 +59,8 @@ struct Params {
   float* dk_acc;            // [B, Lk, H, D]
   float* dv_acc;            // [B, Lk, H, D]
   int32_t init_dq, init_dkv;   // 1: the sums start at zero (the incoming ones are not read)
+  // bias gradient (ra_blockwise_attn_bwd_dbias): per-key sums of dS over the queries, [B, H, Lk]
+  float* dbias_keys;
 };
 
 // ---------------------------------------------------------------- element access
@@ -191,5 +193,7 @@ hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dkdv_step_mfma(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dq_step_mfma(const Params& p, hipStream_t st);
 hipError_t launch_grad_finalize(const float* acc, float factor, void* out, int64_t elems, bool bf16, hipStream_t st);
+hipError_t launch_bias_grad(const float* key_sums, float* dbias, int B, int H, int64_t Lk, int64_t bias_len,
+                            hipStream_t st);
 
 }  // namespace ra

@@ -492,6 +492,31 @@ hipError_t launch_grad_finalize(const float* acc, float factor, void* out, int64
   return hipGetLastError();
 }
 
+// dbias[h, t] = sum over batch rows b and keys j = t, t + bias_len, ... of key_sums[b, h, j]; one
+// lane per (h, t), summing in a fixed order (deterministic)
+__global__ __launch_bounds__(256) void bias_grad_kernel(const float* __restrict__ key_sums, float* __restrict__ dbias,
+                                                        int B, int H, int64_t Lk, int64_t nb) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(H) * nb) return;
+  const int h = static_cast<int>(i / nb);
+  const int64_t t = i % nb;
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const float* row = key_sums + (static_cast<int64_t>(b) * H + h) * Lk;
+    for (int64_t j = t; j < Lk; j += nb) acc += row[j];
+  }
+  dbias[i] = acc;
+}
+
+hipError_t launch_bias_grad(const float* key_sums, float* dbias, int B, int H, int64_t Lk, int64_t bias_len,
+                            hipStream_t st) {
+  const int64_t n = static_cast<int64_t>(H) * bias_len;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(bias_grad_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, key_sums, dbias,
+                     B, H, Lk, bias_len);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_finalize(const Params& p, hipStream_t st) {
   return p.bf16 ? launch_finalize_t<__bf16>(p, st) : launch_finalize_t<float>(p, st);
 }

@@ -219,3 +219,24 @@ def test_bwd_step_validation():
     assert rc == -1 and b"dv" in lib.ra_last_error()
     rc = lib.ra_blockwise_attn_bwd_finalize(FAKE, FAKE, FAKE, FAKE, FAKE, None, ctypes.byref(S(head_dim=72)), None)
     assert rc == -3
+
+
+@needs_cpu
+def test_dbias_validation():
+    lib = _lib()
+    s = api.Shape(1, 2, 64, -1, 1024, 1024, 100, 0.0, api.RA_BF16)
+    need = lib.ra_blockwise_attn_bwd_dbias_workspace_size(ctypes.byref(s))
+    assert need == lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(s)) + 1 * 2 * 1024 * 4
+
+    def call(shape, bias=FAKE, dbias=FAKE, ws=None, ws_bytes=0, dv=None):
+        return lib.ra_blockwise_attn_bwd_dbias(FAKE, FAKE, FAKE, bias, None, 4, 256, 256, 1, FAKE, FAKE, FAKE, FAKE,
+                                               FAKE, dv, dbias, ws, ws_bytes, ctypes.byref(shape), None)
+
+    # dv stays NULL in every call: none can reach a launch
+    assert call(s, dbias=None) == -1 and b"dbias" in lib.ra_last_error()
+    assert call(s, bias=None) == -1
+    assert call(api.Shape(1, 2, 64, -1, 1024, 1024, 100, 0.0, api.RA_F32), dv=None) == -1   # dv checked first
+    assert call(s, dv=FAKE) == -4 and b"workspace" in lib.ra_last_error()
+    assert call(s, dv=FAKE, ws=FAKE, ws_bytes=need - 4) == -4
+    f32 = api.Shape(1, 2, 64, -1, 1024, 1024, 100, 0.0, api.RA_F32)
+    assert call(f32, dv=FAKE, ws=FAKE, ws_bytes=need) == -3

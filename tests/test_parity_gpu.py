@@ -226,3 +226,41 @@ def test_errors_surface_as_exceptions(gpu):
     q96 = torch.zeros(1, 64, 2, 96, dtype=torch.bfloat16, device=gpu)
     with pytest.raises(ra.RAError, match="head_dim"):
         ra.blockwise_attn_fwd(q96, q96, q96, n_ring=1, q_chunk=64, k_chunk=64, causal=True)
+
+
+# ------------------------------------------------------------------ bias gradient
+DBIAS = [
+    ("bias-causal", dict(kv_len=1024, n_ring=4, bias_len=300)),
+    ("bias-seg-noncausal", dict(kv_len=768, n_ring=3, causal=False, bias_len=64, segments="docs", doc_len=(5, 90))),
+    ("bias-rank2-longer-than-keys", dict(kv_len=2048, n_ring=4, ring_rank=2, bias_len=3000)),
+    ("bias-d128-batch2-blocks", dict(head_dim=128, batch=2, heads=3, kv_len=960, n_ring=3, bias_len=100, causal=40,
+                                     segments="scattered")),
+]
+
+
+@pytest.mark.parametrize("name,kw", DBIAS, ids=[c[0] for c in DBIAS])
+def test_bias_gradient(gpu, name, kw):
+    w = W.small(name, backward=True, **kw)
+    t = P.make(w, gpu)
+    out, lse = P.gpu_forward(w, t)
+    kwr = dict(n_ring=w.n_ring, q_chunk=w.q_chunk, k_chunk=w.k_chunk, causal=w.causal, ring_rank=w.ring_rank)
+    dq, dk, dv, db = ra.blockwise_attn_bwd_dbias(t["q"], t["k"], t["v"], out, lse, t["dout"], t["bias"],
+                                                 t["segment_ids"], **kwr)
+    fq, fk, fv = P.gpu_backward(w, t, out, lse)
+    db2 = ra.blockwise_attn_bwd_dbias(t["q"], t["k"], t["v"], out, lse, t["dout"], t["bias"], t["segment_ids"],
+                                      **kwr)[3]
+    torch.cuda.synchronize()
+    # the other gradients are those of the plain backward, bit for bit; dbias is deterministic
+    assert torch.equal(dq, fq) and torch.equal(dk, fk) and torch.equal(dv, fv)
+    assert torch.equal(db, db2)
+    d = P.oracle_inputs(t)
+    import oracle
+    ref = oracle.bias_grad(d["q"], d["k"], d["v"], d["dout"], q_pos=w.q_positions(), causal=w.causal,
+                           bias=d["bias"], segment_ids=d["segment_ids"])
+    got = db.double().cpu().numpy()
+    # float32 sums of bfloat16-rounded products: bound relative to the gradient's own scale
+    err = np.abs(got - ref).max()
+    scale_ = np.abs(ref).max()
+    print(f"{name} dbias: max_abs={err:.3e} max|ref|={scale_:.3g}", flush=True)
+    assert err <= 2e-2 * scale_ + 1e-3, (err, scale_)
+    assert abs(float(got.sum())) <= 1e-2 * np.abs(got).sum() + 1e-3   # scores' gradient sums to zero per row
