@@ -22,6 +22,8 @@ Modules
 ``attention``  the plain definition, softmax(scale*QK^T + bias + mask) V, and
                its gradients, in float64 (``forward``, ``backward``,
                ``bias_grad``, ``probabilities``).
+``ffn``        the blockwise feed-forward (SwiGLU) and its gradients, in
+               float64.
 ``blockwise``  the method's own procedure -- ring-order steps over K/V
                blocks, query/key chunks, online-softmax merge -- in float64,
                used to pin the claim that the procedure is exact.
@@ -33,3 +35,4 @@ library special case, closed forms, finite differences, invariants); none is
 from .attention import (forward, backward, bias_grad, probabilities, query_positions, visible_pairs,  # noqa: F401
                         causal_block)
 from .blockwise import ring_forward  # noqa: F401
+from .ffn import ffn_forward, ffn_backward  # noqa: F401
