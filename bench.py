@@ -74,6 +74,10 @@ def parse():
                          "(one ra_blockwise_attn_fwd_step / _bwd_step per visible ring step, then the "
                          "finalize calls), K/V blocks already in contiguous receive buffers (a sweep line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ffn", action="store_true",
+                    help="time the blockwise SwiGLU feed-forward instead (a sweep line): one device's 131072 tokens, "
+                         "d_model 1024, d_ff 2816, chunks of --ffn-chunk tokens, forward + backward")
+    ap.add_argument("--ffn-chunk", type=int, default=16384, help="tokens per chunk of the blockwise feed-forward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -119,6 +123,66 @@ def cpu_baseline(w, t, target_s):
                       f"host {platform.processor() or platform.machine()}"}
 
 
+def bench_ffn(args):
+    """The blockwise feed-forward on one device's share of the 1M-token context (131072 tokens of the
+    1024-wide model, LLaMA's d_ff rule: 8/3 * 1024 rounded up to a multiple of 256 = 2816)."""
+    import torch
+
+    import long_context_exact_attn_amd as ra
+    from long_context_exact_attn_amd import metrics as M
+    T, d, f, chunk = 131072, 1024, 2816, args.ffn_chunk
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(2024)
+    x = torch.randn((T, d), generator=g, device=dev).to(torch.bfloat16)
+    w1 = (torch.randn((f, d), generator=g, device=dev) / d ** 0.5).to(torch.bfloat16)
+    w3 = (torch.randn((f, d), generator=g, device=dev) / d ** 0.5).to(torch.bfloat16)
+    w2 = (torch.randn((d, f), generator=g, device=dev) / f ** 0.5).to(torch.bfloat16)
+    dout = torch.randn((T, d), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    dws = [torch.empty(w.shape, dtype=torch.float32, device=dev) for w in (w1, w3, w2)]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ra.blockwise_ffn_fwd(x, w1, w3, w2, chunk=chunk, out=out)
+        if ev is not None:
+            ev[1].record()
+        ra.blockwise_ffn_bwd(x, w1, w3, w2, dout, chunk=chunk, dx=dx, dw1=dws[0], dw3=dws[1], dw2=dws[2])
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    unit = T * d * f
+    fl_fwd, fl_bwd = 6 * unit, 12 * unit   # three products forward; six backward (recompute not counted)
+    value = (fl_fwd + fl_bwd) / (ms_step * 1e-3) / 1e12
+    kernels = {"ffn_fwd": {"ms": round(fwd_ms, 4), "tflops": round(fl_fwd / (fwd_ms * 1e-3) / 1e12, 2)},
+               "ffn_bwd": {"ms": round(bwd_ms, 4), "tflops": round(fl_bwd / (bwd_ms * 1e-3) / 1e12, 2)}}
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    line = {"metric": "blockwise feed-forward TFLOP/s (fwd+bwd) at 1 MI355X", "value": round(value, 2),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"blockwise SwiGLU feed-forward, 131072 tokens, d_model 1024, d_ff 2816, "
+                                   f"chunks of {chunk} tokens", "pass": "fwd+bwd"},
+            "frac_peak": round(value / M.PEAK_BF16_TFLOPS, 4), "kernels": kernels,
+            "roofline": {"bound": "mfma", "kernel": dom, "achieved": kernels[dom]["tflops"],
+                         "peak": M.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(kernels[dom]["tflops"] / M.PEAK_BF16_TFLOPS, 4), "traffic": None}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.source_hash:
@@ -128,6 +192,9 @@ def main():
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(the ring's K/V exchange across devices is not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.ffn:
+        bench_ffn(args)
+        return
     import torch
 
     import long_context_exact_attn_amd as ra

@@ -59,8 +59,9 @@
  *    a non-zero return means nothing was launched, and ra_last_error()
  *    describes it.  RA_ERR_HIP reports a failed launch.  Faults during
  *    execution surface at the caller's next synchronisation.
- *  - Thread safety.  Entry points keep no state apart from the per-thread
- *    error string; concurrent calls on different streams are safe.
+ *  - Thread safety.  The attention entry points keep no state apart from the
+ *    per-thread error string; concurrent calls on different streams are safe.
+ *    The feed-forward entry points keep one rocBLAS handle per device.
  */
 #ifndef RA_ATTN_H
 #define RA_ATTN_H
@@ -220,6 +221,33 @@ int ra_blockwise_attn_bwd_step(const void* q, const void* k, const void* v, cons
  * dv = dv_acc [B,Lk,H,D], converted to shape.dtype (scale: shape.scale, or 1/sqrt(head_dim)). */
 int ra_blockwise_attn_bwd_finalize(const float* dq_acc, const float* dk_acc, const float* dv_acc, void* dq, void* dk,
                                    void* dv, const ra_shape* shape, void* stream);
+
+/*
+ * Blockwise feed-forward ("RingAttention核心功能全解析", 快速上手: blockwise_feedforward is
+ * exported next to ringattention; the pages give only its name).  The sharding example of the
+ * same page builds its mesh from LLaMAConfig, so the feed-forward is LLaMA's SwiGLU, per token:
+ *   out = W2 (silu(W1 x) * (W3 x)),   silu(a) = a / (1 + exp(-a)),
+ * computed over chunks of `chunk` tokens so that the [tokens, d_ff] intermediate only ever
+ * exists for one chunk (the result does not depend on the chunk).  bfloat16 tensors, float32
+ * accumulation; the projections W1 x and W3 x, the gated activation h and the gradients of the
+ * intermediate are rounded to bfloat16 between the products.
+ *   x, out, dout, dx: [tokens, d_model];  w1, w3: [d_ff, d_model];  w2: [d_model, d_ff]
+ *   (row-major, a linear layer's [out, in]);  dw1, dw3, dw2: float32, same shapes as the weights.
+ * d_model and d_ff are multiples of 4; chunk * d_ff < 2^31.  The workspace (device, 256-byte
+ * aligned) holds ra_blockwise_ffn_workspace_size(...) bytes (backward = 1 for the backward).
+ * The backward recomputes each chunk's intermediate, writes dx and overwrites dw1, dw3, dw2
+ * with the sums over all tokens.  The GEMMs run on rocBLAS: the library keeps one rocBLAS
+ * handle per device for the life of the process, and calls of these two entry points are
+ * serialised by a lock.
+ */
+size_t ra_blockwise_ffn_workspace_size(int64_t tokens, int32_t d_model, int32_t d_ff, int64_t chunk,
+                                       int32_t backward);
+int ra_blockwise_ffn_fwd(const void* x, const void* w1, const void* w3, const void* w2, void* out, int64_t tokens,
+                         int32_t d_model, int32_t d_ff, int64_t chunk, void* workspace, size_t workspace_bytes,
+                         void* stream);
+int ra_blockwise_ffn_bwd(const void* x, const void* w1, const void* w3, const void* w2, const void* dout, void* dx,
+                         float* dw1, float* dw3, float* dw2, int64_t tokens, int32_t d_model, int32_t d_ff,
+                         int64_t chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Description of the last error on the calling thread ("" after a success). */
 const char* ra_last_error(void);

@@ -60,6 +60,8 @@ def load_library():
         "ra_blockwise_attn_bwd_step": [P, P, P, P, P, I64, I64, I64, I32, P, P, P, P, P, P, I32, I32, SH, P],
         "ra_blockwise_attn_bwd_finalize": [P, P, P, P, P, P, SH, P],
         "ra_blockwise_attn_bwd_dbias": [P, P, P, P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, P, SZ, SH, P],
+        "ra_blockwise_ffn_fwd": [P, P, P, P, P, I64, I32, I32, I64, P, SZ, P],
+        "ra_blockwise_ffn_bwd": [P, P, P, P, P, P, P, P, P, I64, I32, I32, I64, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -68,6 +70,8 @@ def load_library():
     for name in ("ra_blockwise_attn_bwd_workspace_size", "ra_blockwise_attn_bwd_dbias_workspace_size"):
         getattr(lib, name).argtypes = [SH]
         getattr(lib, name).restype = SZ
+    lib.ra_blockwise_ffn_workspace_size.argtypes = [I64, I32, I32, I64, I32]
+    lib.ra_blockwise_ffn_workspace_size.restype = SZ
     lib.ra_last_error.argtypes = []
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_abi_version.argtypes = []
@@ -337,6 +341,53 @@ def blockwise_attn_bwd_finalize(dq_acc, dk_acc, dv_acc, *, dtype=torch.bfloat16,
     _check(lib.ra_blockwise_attn_bwd_finalize(_ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc), _ptr(dq), _ptr(dk), _ptr(dv),
                                               ctypes.byref(shape), _stream(dq_acc.device)))
     return dq, dk, dv
+
+
+def _ffn_args(x, w1, w3, w2):
+    if x.dim() != 2 or w1.dim() != 2 or w1.shape != w3.shape or w2.shape != (w1.shape[1], w1.shape[0]) \
+            or x.shape[1] != w1.shape[1]:
+        raise ValueError("x [tokens, d_model], w1 and w3 [d_ff, d_model], w2 [d_model, d_ff] expected")
+    for name, t in (("x", x), ("w1", w1), ("w3", w3), ("w2", w2)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor")
+    return x.shape[0], x.shape[1], w1.shape[0]
+
+
+def _ffn_workspace(lib, device, tokens, d, f, chunk, backward, workspace):
+    need = int(lib.ra_blockwise_ffn_workspace_size(int(tokens), int(d), int(f), int(chunk), int(backward)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)   # torch aligns to 256 bytes
+    return workspace
+
+
+def blockwise_ffn_fwd(x, w1, w3, w2, *, chunk, out=None, workspace=None):
+    """out = ra_blockwise_ffn_fwd(...): SwiGLU feed-forward of every token, chunk tokens at a time."""
+    lib = load_library()
+    T, d, f = _ffn_args(x, w1, w3, w2)
+    out = torch.empty_like(x) if out is None else out
+    workspace = _ffn_workspace(lib, x.device, T, d, f, chunk, False, workspace)
+    _check(lib.ra_blockwise_ffn_fwd(_ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out), int(T), int(d), int(f),
+                                    int(chunk), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(x.device)))
+    return out
+
+
+def blockwise_ffn_bwd(x, w1, w3, w2, dout, *, chunk, dx=None, dw1=None, dw3=None, dw2=None, workspace=None):
+    """dx, dw1, dw3, dw2 = ra_blockwise_ffn_bwd(...): dx bfloat16, weight gradients float32."""
+    lib = load_library()
+    T, d, f = _ffn_args(x, w1, w3, w2)
+    if dout.shape != x.shape or dout.dtype != torch.bfloat16 or not dout.is_cuda or not dout.is_contiguous():
+        raise ValueError("dout must be a contiguous bfloat16 GPU tensor shaped like x")
+    dx = torch.empty_like(x) if dx is None else dx
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dw1 = torch.empty(w1.shape, **f32) if dw1 is None else dw1
+    dw3 = torch.empty(w3.shape, **f32) if dw3 is None else dw3
+    dw2 = torch.empty(w2.shape, **f32) if dw2 is None else dw2
+    workspace = _ffn_workspace(lib, x.device, T, d, f, chunk, True, workspace)
+    _check(lib.ra_blockwise_ffn_bwd(_ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(dout), _ptr(dx), _ptr(dw1),
+                                    _ptr(dw3), _ptr(dw2), int(T), int(d), int(f), int(chunk), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(x.device)))
+    return dx, dw1, dw3, dw2
 
 
 def default_scale(head_dim):

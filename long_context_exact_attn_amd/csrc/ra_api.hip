@@ -167,6 +167,73 @@ extern "C" {
 
 int32_t ra_abi_version(void) { return 1; }
 
+static int ffn_check(int64_t tokens, int32_t d_model, int32_t d_ff, int64_t chunk) {
+  if (tokens < 0 || tokens >= kMaxPos) return fail(RA_ERR_SHAPE, "tokens must be in [0, 2^30) (got %lld)", (long long)tokens);
+  if (d_model < 4 || d_ff < 4 || d_model % 4 || d_ff % 4 || d_model > 65536 || d_ff > 262144)
+    return fail(RA_ERR_SHAPE, "d_model and d_ff must be multiples of 4 in [4, 65536] / [4, 262144] (got %d, %d)",
+                d_model, d_ff);
+  if (chunk < 1) return fail(RA_ERR_ARG, "chunk must be >= 1 (got %lld)", (long long)chunk);
+  const int64_t c = tokens < chunk ? tokens : chunk;
+  if (static_cast<int64_t>(d_ff) * c >= (int64_t(1) << 31))
+    return fail(RA_ERR_SHAPE, "chunk * d_ff must stay below 2^31 (chunk %lld, d_ff %d)", (long long)c, d_ff);
+  return RA_OK;
+}
+
+size_t ra_blockwise_ffn_workspace_size(int64_t tokens, int32_t d_model, int32_t d_ff, int64_t chunk, int32_t backward) {
+  if (tokens < 0 || d_model < 1 || d_ff < 1 || chunk < 1) return 0;
+  return ra::ffn_workspace(tokens, d_model, d_ff, chunk, backward != 0).bytes;
+}
+
+int ra_blockwise_ffn_fwd(const void* x, const void* w1, const void* w3, const void* w2, void* out, int64_t tokens,
+                         int32_t d_model, int32_t d_ff, int64_t chunk, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  RA_TRY(ffn_check(tokens, d_model, d_ff, chunk));
+  const int64_t xe = tokens * d_model, we = static_cast<int64_t>(d_ff) * d_model;
+  RA_TRY(need_ptr(x, xe, "x", 2));
+  RA_TRY(need_ptr(out, xe, "out", 2));
+  RA_TRY(need_ptr(w1, we, "w1", 2));
+  RA_TRY(need_ptr(w3, we, "w3", 2));
+  RA_TRY(need_ptr(w2, we, "w2", 2));
+  if (tokens == 0) return ok();
+  const size_t need = ra::ffn_workspace(tokens, d_model, d_ff, chunk, false).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (!aligned(workspace, 256)) return fail(RA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  return hip_status(ra::ffn_forward(static_cast<const __bf16*>(x), static_cast<const __bf16*>(w1),
+                                    static_cast<const __bf16*>(w3), static_cast<const __bf16*>(w2),
+                                    static_cast<__bf16*>(out), tokens, d_model, d_ff, chunk,
+                                    static_cast<char*>(workspace), static_cast<hipStream_t>(stream)),
+                    "feed-forward launch");
+}
+
+int ra_blockwise_ffn_bwd(const void* x, const void* w1, const void* w3, const void* w2, const void* dout, void* dx,
+                         float* dw1, float* dw3, float* dw2, int64_t tokens, int32_t d_model, int32_t d_ff,
+                         int64_t chunk, void* workspace, size_t workspace_bytes, void* stream) {
+  RA_TRY(ffn_check(tokens, d_model, d_ff, chunk));
+  const int64_t xe = tokens * d_model, we = static_cast<int64_t>(d_ff) * d_model;
+  RA_TRY(need_ptr(x, xe, "x", 2));
+  RA_TRY(need_ptr(dout, xe, "dout", 2));
+  RA_TRY(need_ptr(dx, xe, "dx", 2));
+  RA_TRY(need_ptr(w1, we, "w1", 2));
+  RA_TRY(need_ptr(w3, we, "w3", 2));
+  RA_TRY(need_ptr(w2, we, "w2", 2));
+  RA_TRY(need_ptr(dw1, we, "dw1", 4));
+  RA_TRY(need_ptr(dw3, we, "dw3", 4));
+  RA_TRY(need_ptr(dw2, we, "dw2", 4));
+  const size_t need = tokens ? ra::ffn_workspace(tokens, d_model, d_ff, chunk, true).bytes : 0;
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (need && !aligned(workspace, 256)) return fail(RA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  return hip_status(ra::ffn_backward(static_cast<const __bf16*>(x), static_cast<const __bf16*>(w1),
+                                     static_cast<const __bf16*>(w3), static_cast<const __bf16*>(w2),
+                                     static_cast<const __bf16*>(dout), static_cast<__bf16*>(dx), dw1, dw3, dw2,
+                                     tokens, d_model, d_ff, chunk, static_cast<char*>(workspace),
+                                     static_cast<hipStream_t>(stream)),
+                    "feed-forward backward launch");
+}
+
 const char* ra_last_error(void) { return g_last_error.c_str(); }
 
 int ra_blockwise_attn_fwd(const void* q, const void* k, const void* v, const float* bias,

@@ -193,6 +193,16 @@ hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dkdv_step_mfma(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dq_step_mfma(const Params& p, hipStream_t st);
 hipError_t launch_grad_finalize(const float* acc, float factor, void* out, int64_t elems, bool bf16, hipStream_t st);
+// blockwise feed-forward (ffn.hip): workspace regions (byte offsets) for one chunk of tokens
+struct FfnWorkspace {
+  size_t w13, gu, h, dh, dgdu, dw13, bytes;
+};
+FfnWorkspace ffn_workspace(int64_t tokens, int d_model, int d_ff, int64_t chunk, bool backward);
+hipError_t ffn_forward(const __bf16* x, const __bf16* w1, const __bf16* w3, const __bf16* w2, __bf16* out,
+                       int64_t tokens, int d, int f, int64_t chunk, char* ws, hipStream_t st);
+hipError_t ffn_backward(const __bf16* x, const __bf16* w1, const __bf16* w3, const __bf16* w2, const __bf16* dout,
+                        __bf16* dx, float* dw1, float* dw3, float* dw2, int64_t tokens, int d, int f, int64_t chunk,
+                        char* ws, hipStream_t st);
 hipError_t launch_bias_grad(const float* key_sums, float* dbias, int B, int H, int64_t Lk, int64_t bias_len,
                             hipStream_t st);
 

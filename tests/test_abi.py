@@ -240,3 +240,25 @@ def test_dbias_validation():
     assert call(s, dv=FAKE, ws=FAKE, ws_bytes=need - 4) == -4
     f32 = api.Shape(1, 2, 64, -1, 1024, 1024, 100, 0.0, api.RA_F32)
     assert call(f32, dv=FAKE, ws=FAKE, ws_bytes=need) == -3
+
+
+@needs_cpu
+def test_ffn_validation():
+    lib = _lib()
+    # at least the chunk's gate/up projections and activation, bfloat16
+    assert lib.ra_blockwise_ffn_workspace_size(1000, 256, 704, 512, 0) >= 512 * 704 * (2 + 2 + 2)
+    assert lib.ra_blockwise_ffn_workspace_size(1000, 256, 704, 512, 1) > lib.ra_blockwise_ffn_workspace_size(
+        1000, 256, 704, 512, 0)
+
+    def fwd(T=64, d=64, f=96, chunk=16, out=None, ws=None, ws_bytes=0):
+        return lib.ra_blockwise_ffn_fwd(FAKE, FAKE, FAKE, FAKE, out, T, d, f, chunk, ws, ws_bytes, None)
+
+    assert fwd(d=66) == -2
+    assert fwd(f=0) == -2
+    assert fwd(chunk=0) == -1
+    assert fwd(T=-1) == -2
+    assert fwd() == -1 and b"out" in lib.ra_last_error()
+    assert fwd(out=FAKE) == -4 and b"workspace" in lib.ra_last_error()
+    assert fwd(T=0) == 0   # nothing to do, nothing launched
+    rc = lib.ra_blockwise_ffn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 64, 96, 16, None, 0, None)
+    assert rc == -1 and b"dw2" in lib.ra_last_error()
