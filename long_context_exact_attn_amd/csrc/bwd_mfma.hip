@@ -12,10 +12,16 @@
 //   buffers deep.  Per query tile and 32-query block:
 //     S  = Q . K^T,  dP = dO . V^T     (rows = queries, columns = the lane's key)
 //     P  = exp2(S * scale * log2e + bias - lse * log2e),  dS = P (dP - Delta)
+//   The held K rows are stored pre-multiplied by scale * log2e (rounded to bfloat16) and the
+//   score accumulators start at bias - lse * log2e, the dP accumulators at -Delta, so that the
+//   matrix unit delivers the exponent and dP - Delta directly and the vector unit is left with
+//   one exponential and one product per score.
 //     dV^T += dO^T . P,  dK^T += Q^T . dS     (dO^T, Q^T by transposing LDS reads)
 // dQ kernel -- the forward's tiling: one workgroup owns a query tile (Q, dO,
 //   lse, Delta in VGPRs) and K/V tiles stream through LDS in ring order:
 //     S^T = K . Q^T,  dP^T = V . dO^T,  dS^T as above,  dQ^T += K^T . dS^T
+//   with the same folding: Q held pre-multiplied by scale * log2e, accumulators started at
+//   bias - lse * log2e and -Delta.
 #include "mfma_util.cuh"
 
 
@@ -95,7 +101,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     for (int kk = 0; kk < KK; ++kk) {
       const bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + off + 16 * kk + 8 * hh);
       const bf16x8 y = *reinterpret_cast<const bf16x8*>(gp + off + 16 * kk + 8 * hh);
-      Qf[nb][kk] = ok ? x : bf16x8{};
+      Qf[nb][kk] = ok ? scale_bf16x8(x, p.scale * kLog2e) : bf16x8{};
       Gf[nb][kk] = ok ? y : bf16x8{};
     }
     const int64_t li = (static_cast<int64_t>(b) * p.H + h) * p.Lq + qrow_base + (ok ? row : 0);
@@ -118,7 +124,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     wg_id_range(lo, hi, sWaveSeg, wave, lane, gseg_lo, gseg_hi);
   }
 
-  const float c = p.scale * kLog2e;
+  // starting values of the score and dP accumulators: -lse * log2e and -Delta of the lane's query
+  // (with a bias the score start is formed per tile, bias - lse * log2e)
+  f32x16 s_init[NQB], g_init[NQB];
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s_init[nb][v] = -lse2[nb];
+      g_init[nb][v] = -dlt[nb];
+    }
   f32x16 dQ[DB][NQB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -260,8 +275,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NQB; ++nb) {
-          S[mb][nb] = f32x16{};
-          G[mb][nb] = f32x16{};
+          if constexpr (HAS_BIAS) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              S[mb][nb][v] = sBias[buf][mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3)] + s_init[nb][v];
+          } else {
+            S[mb][nb] = s_init[nb];
+          }
+          G[mb][nb] = g_init[nb];
         }
       // a raised wave priority while the score products issue keeps the matrix unit fed
       // while the other wave on the SIMD does its exponentials (measured: ~2% on dQ)
@@ -329,11 +350,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
               const int v = 8 * st + i;
-              const int kr = mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-              const float y = HAS_BIAS ? __builtin_fmaf(S[mb][nb][v], c, sBias[buf][kr] - lse2[nb])
-                                       : __builtin_fmaf(S[mb][nb][v], c, -lse2[nb]);
-              const float pr = __builtin_amdgcn_exp2f(y);
-              e[i] = pr * (G[mb][nb][v] - dlt[nb]);
+              e[i] = __builtin_amdgcn_exp2f(S[mb][nb][v]) * G[mb][nb][v];
             }
             dS[nb][mb][st] = pack_bf16x8(e);
           }
@@ -441,7 +458,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   __shared__ __attribute__((aligned(16))) __bf16 sQ[NS][TILE];
   __shared__ __attribute__((aligned(16))) __bf16 sG[NS][TILE];
   __shared__ __attribute__((aligned(16))) float sL[NS][BQ];    // -lse * log2e (-inf: row contributes nothing)
-  __shared__ __attribute__((aligned(16))) float sDl[NS][BQ];   // Delta
+  __shared__ __attribute__((aligned(16))) float sDl[NS][BQ];   // -Delta
   __shared__ __attribute__((aligned(16))) int sSg[NS][BQ];     // segment id of the query
   __shared__ int sWaveSeg[kWaves][2];
 
@@ -472,7 +489,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   // segment ids on positions relative to the keys held (kv_pos0 = 0 outside a ring step)
   const int* __restrict__ ids = HAS_SEG ? p.seg + static_cast<int64_t>(b) * p.seg_len + p.kv_pos0 : nullptr;
 
-  // the wave's keys, as B operands of S = Q . K^T and dP = dO . V^T
+  // the wave's keys, as B operands of S = Q . K^T (K times scale * log2e) and dP = dO . V^T
   bf16x8 Kf[NKB][KK], Vf[NKB][KK];
   float kbias[NKB];
   int ksg[NKB];
@@ -486,7 +503,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     for (int kk = 0; kk < KK; ++kk) {
       const bf16x8 x = *reinterpret_cast<const bf16x8*>(kp + off + 16 * kk + 8 * hh);
       const bf16x8 y = *reinterpret_cast<const bf16x8*>(vp + off + 16 * kk + 8 * hh);
-      Kf[kb][kk] = ok ? x : bf16x8{};
+      Kf[kb][kk] = ok ? scale_bf16x8(x, p.scale * kLog2e) : bf16x8{};
       Vf[kb][kk] = ok ? y : bf16x8{};
     }
     kbias[kb] = (HAS_BIAS && ok) ? p.bias[static_cast<int64_t>(h) * p.bias_len + (p.kv_pos0 + key) % p.bias_len] * kLog2e
@@ -506,7 +523,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     wg_id_range(lo, hi, sWaveSeg, wave, lane, gseg_lo, gseg_hi);
   }
 
-  const float c = p.scale * kLog2e;
   // with a bias (outside ring steps): the lane's part of sum_i dS_ij for its key, the bias gradient
   constexpr bool KEYSUM = HAS_BIAS && !STEP;
   float dsum[NKB];
@@ -579,7 +595,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   auto store_small = [&](int slot) {
     if (tid < BQ) {
       sL[slot][tid] = (lok && lreg != -INFINITY) ? -lreg * kLog2e : -INFINITY;
-      sDl[slot][tid] = lok ? dreg : 0.f;
+      sDl[slot][tid] = lok ? -dreg : 0.f;
       if constexpr (HAS_SEG) sSg[slot][tid] = lok ? sreg : 0;
     }
   };
@@ -676,23 +692,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       }
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb) {
-        f32x16 S[NKB], G[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          S[kb] = f32x16{};
-          G[kb] = f32x16{};
-        }
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 aq = lds_read_swz<D>(Qt, qb * 32 + l32, 2 * kk + hh);
-          const bf16x8 ag = lds_read_swz<D>(Gt, qb * 32 + l32, 2 * kk + hh);
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            S[kb] = mfma32(aq, Kf[kb][kk], S[kb]);
-            G[kb] = mfma32(ag, Vf[kb][kk], G[kb]);
-          }
-        }
-        // the 16 query rows this lane holds: qr(v) = qb*32 + 8*(v/4) + 4*hh + v%4
+        // the 16 query rows this lane holds: qr(v) = qb*32 + 8*(v/4) + 4*hh + v%4;
+        // -lse * log2e and -Delta of each start the accumulators
         float nl[16], dl[16];
         int qs[16];
 #pragma unroll
@@ -711,6 +712,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
             qs[4 * g4 + 1] = z.y;
             qs[4 * g4 + 2] = z.z;
             qs[4 * g4 + 3] = z.w;
+          }
+        }
+        f32x16 S[NKB], G[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            S[kb][v] = HAS_BIAS ? nl[v] + kbias[kb] : nl[v];
+            G[kb][v] = dl[v];
+          }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 aq = lds_read_swz<D>(Qt, qb * 32 + l32, 2 * kk + hh);
+          const bf16x8 ag = lds_read_swz<D>(Gt, qb * 32 + l32, 2 * kk + hh);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            S[kb] = mfma32(aq, Kf[kb][kk], S[kb]);
+            G[kb] = mfma32(ag, Vf[kb][kk], G[kb]);
           }
         }
         // masked scores become -inf (then P = 0) in a pass of their own, so that tiles
@@ -736,10 +755,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
               const int v = 8 * st + i;
-              const float y = HAS_BIAS ? __builtin_fmaf(S[kb][v], c, kbias[kb] + nl[v]) : __builtin_fmaf(S[kb][v], c, nl[v]);
-              const float pr = __builtin_amdgcn_exp2f(y);
+              const float pr = __builtin_amdgcn_exp2f(S[kb][v]);
               pe[i] = pr;
-              de[i] = pr * (G[kb][v] - dl[v]);
+              de[i] = pr * G[kb][v];
             }
             Pb[kb][st] = pack_bf16x8(pe);
             Sb[kb][st] = pack_bf16x8(de);

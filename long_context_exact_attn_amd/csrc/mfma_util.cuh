@@ -108,6 +108,15 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* e) {
   return r;
 }
 
+// c * x for eight bfloat16 values, rounded to nearest even: folds a constant factor
+// into an operand that stays in registers.
+__device__ __forceinline__ bf16x8 scale_bf16x8(bf16x8 x, float c) {
+  float e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = c * static_cast<float>(x[i]);
+  return pack_bf16x8(e);
+}
+
 // Reductions over the lane pair (l, l ^ 32) that shares one column of a C
 // accumulator: v_permlane32_swap exchanges the two halves of the wave, and
 // both results of the swap hold one value of each pair.
