@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   for (int jj = 0; jj < NSEG; ++jj) {
     const int byte = (wave * NSEG + jj) * 1024 + lane * 16;
     const int row = byte / (2 * D);
-    const int chunk = ((byte % (2 * D)) >> 4) ^ (row & 7);
+    const int chunk = ((byte % (2 * D)) >> 4) ^ swz_key<D>(row);
     grow_[jj] = row;
     goff[jj] = row * static_cast<int>(kstride) + chunk * 8;   // < 64 * H * D, checked on the host
     goff0[jj] = chunk * 8;
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   for (int jj = 0; jj < NSEG; ++jj) {
     const int byte = (wave * NSEG + jj) * 1024 + lane * 16;
     const int row = byte / (2 * D);
-    const int chunk = ((byte % (2 * D)) >> 4) ^ (row & 7);
+    const int chunk = ((byte % (2 * D)) >> 4) ^ swz_key<D>(row);
     grow_[jj] = row;
     goff[jj] = row * static_cast<int>(qstride) + chunk * 8;   // < 64 * H * D, checked on the host
     goff0[jj] = chunk * 8;

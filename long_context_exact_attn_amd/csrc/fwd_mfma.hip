@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   for (int j = 0; j < NSEG; ++j) {
     const int byte = (wave * NSEG + j) * 1024 + lane * 16;
     const int row = byte / (2 * D);
-    const int chunk = ((byte % (2 * D)) >> 4) ^ (row & 7);
+    const int chunk = ((byte % (2 * D)) >> 4) ^ swz_key<D>(row);
     grow_[j] = row;
     goff[j] = row * static_cast<int>(kstride) + chunk * 8;   // < 64 * H * D, checked on the host
     goff0[j] = chunk * 8;

@@ -49,14 +49,30 @@ __device__ __forceinline__ bf16x8 lds_read_a_transposed(const __bf16* tile, int 
   return a;
 }
 
-// ---- swizzled unpadded tiles: a row of D bf16 holds D / 8 chunks of 16 bytes, and
-// chunk c of row r is stored at chunk position c ^ (r & 7).  Eight consecutive rows
-// then spread any one chunk over eight distinct positions, so the 16-byte operand
-// reads of 8 lanes (rows r..r+7) and the transposing reads below touch distinct banks,
-// without padding (which direct global -> LDS loads cannot produce).
+// ---- swizzled unpadded tiles.  A row of D bf16 holds D / 8 chunks of 16 bytes, and
+// chunk c of row r is stored at chunk position c ^ swz_key<D>(r).  gfx950's LDS has 64
+// banks of 4 bytes (256 bytes per cycle), so
+//   - a 16-byte operand read (lds_read_swz) is served 16 lanes at a time: 16 consecutive
+//     rows (aligned to 16), one chunk each;
+//   - a transposing 8-byte read is served 32 lanes at a time: 4 consecutive rows (aligned to
+//     4), 4 consecutive chunks (aligned to 4), both halves of each.
+// Each group must cover the 256-byte bank period exactly once.  At D = 64 two rows share a
+// period (row parity picks the half), so the key must map the 8 rows of one parity among 16
+// to 8 distinct values and give rows r and r + 2 of an aligned 4 different bit 2: key = (bit 1,
+// bit 2, bit 3) of r.  At D = 128 a row fills the period, so the key must be a bijection over 16
+// rows whose bits 3..2 differ within an aligned 4: key = (bits 1..0, bits 3..2) of r.
+// (r & 7, the usual key for 32 banks, leaves every such read two-way conflicted here.)  Direct global -> LDS copies write 16 consecutive bytes
+// per lane and fetch the global chunk that belongs there, so they are conflict-free for any key.
+template <int D>
+__device__ __forceinline__ int swz_key(int row) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
+  else return ((row & 3) << 2) | ((row >> 2) & 3);
+}
+
 template <int D>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * D + ((chunk ^ (row & 7)) << 3);
+  return row * D + ((chunk ^ swz_key<D>(row)) << 3);
 }
 
 // 16-byte operand read of row `row`, chunk `chunk` of a swizzled tile.

@@ -1,7 +1,7 @@
 // Issue-rate microbenchmarks for gfx950, used to set the ceilings the attention kernels are
 // judged against: sustained v_mfma_f32_32x32x16_bf16 throughput, cycles per wave64
 // instruction of v_exp_f32, v_fma_f32, v_dot2_f32_bf16 and v_max, and whether exponentials
-// issued between matrix products of one wave overlap them.  Every thread writes one float
+// issued between matrix products of one wave overlap them, and LDS read bandwidth.  Every thread writes one float
 // of `out` (sized for the largest grid); nothing else is read or written.
 #include <hip/hip_runtime.h>
 #include <cstdio>
@@ -98,6 +98,45 @@ __global__ __launch_bounds__(512) void k_split(float* out, float seed, int n_mfm
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// LDS read bandwidth with the attention kernels' operand patterns on a 64-column bf16 tile
+// whose 16-byte chunks are XOR-swizzled by row: MODE 0 reads 16 bytes per lane (row l % 32,
+// chunk 2 kk + l / 32), MODE 1 the two 8-byte transposing reads of one transposed operand.
+// Each wave reads its own rows of a 32 KiB buffer; the loaded words are folded with xor.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+template <int MODE>
+__global__ __launch_bounds__(256) void k_lds(float* out, int n) {
+  __shared__ __attribute__((aligned(16))) __bf16 buf[16384];
+  for (int i = threadIdx.x; i < 16384; i += 256) buf[i] = (__bf16)(float)(i & 255);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
+  unsigned acc = 0;
+  for (int it = 0; it < n; ++it) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = ((it * 4 + u) & 15) * 1024 + w * 256;   // (element offset of a 64-row tile region) < 16384
+      const __bf16* tile = buf + (t & 8191);                  // tiles of 64 x 64 start below 8192 + 4096
+      if (MODE == 0) {
+        const int row = l32, chunk = (2 * u + hh) & 7;
+        const uint4 x = *reinterpret_cast<const uint4*>(tile + row * 64 + ((chunk ^ (row & 7)) << 3));
+        acc ^= x.x ^ x.y ^ x.z ^ x.w;
+      } else {
+        const int g = lane >> 4, gi = lane & 15;
+        const int row = (u & 1) * 16 + 4 * hh + (gi >> 2);
+        const int col = (u >> 1) * 32 + 16 * (g & 1) + 4 * (gi & 3);
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const __bf16* p0 = tile + row * 64 + (((col >> 3) ^ (row & 7)) << 3) + (col & 7);
+        const __bf16* p1 = tile + (row + 8) * 64 + (((col >> 3) ^ ((row + 8) & 7)) << 3) + (col & 7);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+        acc ^= (unsigned)(unsigned short)lo[0] ^ ((unsigned)(unsigned short)lo[1] << 16) ^ (unsigned)(unsigned short)lo[2] ^
+               ((unsigned)(unsigned short)lo[3] << 16) ^ (unsigned)(unsigned short)hi[0] ^
+               ((unsigned)(unsigned short)hi[1] << 16) ^ (unsigned)(unsigned short)hi[2] ^ ((unsigned)(unsigned short)hi[3] << 16);
+      }
+    }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = (float)acc;
+}
+
 #define CHECK(x)                                                                  \
   do {                                                                            \
     hipError_t e_ = (x);                                                          \
@@ -173,6 +212,18 @@ int main() {
              op == 0 ? "exp" : "fma", N, tm, nv, op == 0 ? "exp" : "fma", tv, tb, tm + tv, tm > tv ? tm : tv);
     }
   }
+  for (int mode = 0; mode < 2; ++mode)
+    for (int wpc : {1, 2}) {   // 4 or 8 waves per CU
+      const int g = cus * wpc;
+      const int n = 4096;
+      float ms = timeit([&] {
+        if (mode == 0) hipLaunchKernelGGL(k_lds<0>, dim3(g), dim3(256), 0, 0, out, n);
+        else hipLaunchKernelGGL(k_lds<1>, dim3(g), dim3(256), 0, 0, out, n);
+      });
+      const double bytes = double(g) * 4 * n * 4 * 1024;   // every operand read moves 1 KiB per wave
+      printf("lds %s wg/CU=%d: %.3f ms, %.1f bytes/clk/CU at 2.4 GHz\n", mode == 0 ? "ds_read_b128" : "2x ds_read_b64_tr_b16",
+             wpc, ms, bytes / (ms * 1e-3 * 2.4e9) / cus);
+    }
   CHECK(hipFree(out));
   return 0;
 }
