@@ -87,7 +87,7 @@ typedef enum ra_status {
 /* Problem description shared by all calls (48 bytes, no padding). */
 typedef struct ra_shape {
   int32_t batch;      /* B >= 0 */
-  int32_t heads;      /* H >= 0 */
+  int32_t heads;      /* H >= 0, with heads * head_dim < 2^24 */
   int32_t head_dim;   /* D: 64 or 128 */
   int32_t ring_rank;  /* -1: all blocks; r in [0, n_ring): one rank's query block */
   int64_t q_len;      /* Lq */

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
 #ifndef RA_DQ_NS
-#define RA_DQ_NS 2
+#define RA_DQ_NS 3
 #endif
   constexpr int NS = D == 64 ? RA_DQ_NS : 2;  // LDS stages of the K/V ring
   constexpr int TILE = BK * D;         // unpadded, swizzled
@@ -431,9 +431,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 
 // ================================================================== dK/dV (K/V tiles stationary)
 #ifndef RA_KV_BQ
-#define RA_KV_BQ 64
+#define RA_KV_BQ 128
 #endif
-constexpr int kBqKv = RA_KV_BQ;   // queries per LDS tile
+constexpr int kBqKv = RA_KV_BQ;   // queries per LDS tile at head_dim 64 without segment ids (else 64)
 
 // STEP: one backward ring step (ra_blockwise_attn_bwd_step): the queries held are one block at
 // global positions q_pos0 + i, and dK / dV are summed into float32 caller memory (unscaled).
@@ -441,7 +441,7 @@ template <int D, int NKB, int CM, bool HAS_BIAS, bool HAS_SEG, int OCC, bool STE
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void dkdv_mfma_kernel(Params p) {
   constexpr bool CAUSAL = CM != 0;
   constexpr bool CBLK = CM == 2;
-  constexpr int BQ = kBqKv;
+  constexpr int BQ = (HAS_SEG || D != 64) ? 64 : kBqKv;
   constexpr int KW = 32 * NKB;         // keys per wave
   constexpr int BKW = kWaves * KW;     // keys per workgroup
   constexpr int KK = D / 16;
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     const int row = byte / (2 * D);
     const int chunk = ((byte % (2 * D)) >> 4) ^ swz_key<D>(row);
     grow_[jj] = row;
-    goff[jj] = row * static_cast<int>(qstride) + chunk * 8;   // < 64 * H * D, checked on the host
+    goff[jj] = row * static_cast<int>(qstride) + chunk * 8;   // < 128 * H * D, checked on the host
     goff0[jj] = chunk * 8;
   }
   // (raw values are kept until the store, so that the wait for these loads lands there and
@@ -624,7 +624,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   auto next_tile = [&]() -> bool {
     while (walk.next<BQ>()) {
       if constexpr (!HAS_SEG) return true;
-      static_assert(BQ == 64, "the segment filter works in 64-query tiles");
+      static_assert(!HAS_SEG || BQ == 64, "the segment filter works in 64-query tiles");
       // local rows of the current rank: the id of row q sits at position pos_base + q
       const int skip = filt.skip(ids + walk.pos_base, walk.row0, walk.rend, gseg_lo, gseg_hi, lane);
       if (skip == 0) return true;
@@ -722,6 +722,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
             S[kb][v] = HAS_BIAS ? nl[v] + kbias[kb] : nl[v];
             G[kb][v] = dl[v];
           }
+        // raised wave priority while the score products issue (as in dQ)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const bf16x8 aq = lds_read_swz<D>(Qt, qb * 32 + l32, 2 * kk + hh);
@@ -732,6 +734,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
             G[kb] = mfma32(ag, Vf[kb][kk], G[kb]);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
         // masked scores become -inf (then P = 0) in a pass of their own, so that tiles
         // without masks run the loop below with no selects
         if (need_mask) {
