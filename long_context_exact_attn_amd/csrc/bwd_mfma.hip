@@ -55,6 +55,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   __shared__ __attribute__((aligned(16))) __bf16 sV[NS][TILE];
   __shared__ float sBias[NS][BK];
   __shared__ __attribute__((aligned(16))) int sSeg[NS][BK];
+  __shared__ int sSegRange[NS][2];   // smallest and largest segment id among the tile's keys
   __shared__ int sWaveSeg[kWaves][2];
 
   const int tid = threadIdx.x;
@@ -111,8 +112,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     dlt[nb] = ok ? p.delta[li] : 0.f;
     qseg[nb] = (HAS_SEG && ok) ? ids[wpos0 + nb * 32 + l32] : 0;
   }
-  // the workgroup's range of query segment ids: K/V tiles with no key id in it are passed over
-  int gseg_lo = 0, gseg_hi = 0;
+  // the wave's and the workgroup's range of query segment ids: K/V tiles with no key id in the
+  // workgroup's range are passed over, and a wave skips the products of a tile with none in its own
+  int gseg_lo = 0, gseg_hi = 0, qseg_lo = 0, qseg_hi = 0;
   if constexpr (HAS_SEG) {
     int lo = INT32_MAX, hi = INT32_MIN;
 #pragma unroll
@@ -121,7 +123,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         lo = min(lo, qseg[nb]);
         hi = max(hi, qseg[nb]);
       }
-    wg_id_range(lo, hi, sWaveSeg, wave, lane, gseg_lo, gseg_hi);
+    qseg_lo = __builtin_amdgcn_readfirstlane(wave_min_i32(lo));
+    qseg_hi = __builtin_amdgcn_readfirstlane(wave_max_i32(hi));
+    wg_id_range(qseg_lo, qseg_hi, sWaveSeg, wave, lane, gseg_lo, gseg_hi);
   }
 
   // starting values of the score and dP accumulators: -lse * log2e and -Delta of the lane's query
@@ -189,7 +193,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   auto store_small = [&](int slot) {
     if (tid < BK) {
       if constexpr (HAS_BIAS) sBias[slot][tid] = kok ? breg * kLog2e : 0.f;
-      if constexpr (HAS_SEG) sSeg[slot][tid] = kok ? sreg : 0;
+      if constexpr (HAS_SEG) {
+        const int sid = kok ? sreg : 0;
+        sSeg[slot][tid] = sid;
+        const int lo = wave_min_i32(kok ? sid : INT32_MAX);   // BK = 64: one wave holds the tile
+        const int hi = wave_max_i32(kok ? sid : INT32_MIN);
+        if (tid == 0) {
+          sSegRange[slot][0] = lo;
+          sSegRange[slot][1] = hi;
+        }
+      }
     }
   };
   auto issue_kv = [&](int key0, int kend, int slot) {
@@ -268,7 +281,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 
     const __bf16* Kt = sK[buf];
     const __bf16* Vt = sV[buf];
-    const bool wave_active = wlast >= 0 && !(CAUSAL && key0 > (CBLK ? wlim_last : wpos + wlast));
+    bool wave_active = wlast >= 0 && !(CAUSAL && key0 > (CBLK ? wlim_last : wpos + wlast));
+    bool seg_mask = HAS_SEG;   // some pair of the tile may lie in different segments
+    if constexpr (HAS_SEG) {
+      const int klo = __builtin_amdgcn_readfirstlane(sSegRange[buf][0]);
+      const int khi = __builtin_amdgcn_readfirstlane(sSegRange[buf][1]);
+      wave_active = wave_active && klo <= qseg_hi && khi >= qseg_lo;
+      seg_mask = !(klo == khi && qseg_lo == qseg_hi && klo == qseg_lo);
+    }
     if (wave_active) {
       f32x16 S[2][NQB], G[2][NQB];
 #pragma unroll
@@ -302,9 +322,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       }
       __builtin_amdgcn_s_setprio(0);
 
-      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > (CBLK ? wlim_first : wpos));
+      const bool need_mask = seg_mask || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > (CBLK ? wlim_first : wpos));
       int kseg[2][16];
-      if constexpr (HAS_SEG) {
+      if (HAS_SEG && need_mask) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -460,6 +480,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   __shared__ __attribute__((aligned(16))) float sL[NS][BQ];    // -lse * log2e (-inf: row contributes nothing)
   __shared__ __attribute__((aligned(16))) float sDl[NS][BQ];   // -Delta
   __shared__ __attribute__((aligned(16))) int sSg[NS][BQ];     // segment id of the query
+  __shared__ int sTileSeg[NS][2];   // smallest and largest segment id among the tile's queries
   __shared__ int sWaveSeg[kWaves][2];
 
   const int tid = threadIdx.x;
@@ -510,8 +531,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
                                  : 0.f;
     ksg[kb] = (HAS_SEG && ok) ? ids[key] : 0;
   }
-  // the workgroup's range of key segment ids: query tiles with no id in it are passed over
-  int gseg_lo = 0, gseg_hi = 0;
+  // the wave's and the workgroup's range of key segment ids: query tiles with no id in the
+  // workgroup's range are passed over, and a wave skips the products of a tile with none in its own
+  int gseg_lo = 0, gseg_hi = 0, kseg_lo = 0, kseg_hi = 0;
   if constexpr (HAS_SEG) {
     int lo = INT32_MAX, hi = INT32_MIN;
 #pragma unroll
@@ -520,7 +542,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         lo = min(lo, ksg[kb]);
         hi = max(hi, ksg[kb]);
       }
-    wg_id_range(lo, hi, sWaveSeg, wave, lane, gseg_lo, gseg_hi);
+    kseg_lo = __builtin_amdgcn_readfirstlane(wave_min_i32(lo));
+    kseg_hi = __builtin_amdgcn_readfirstlane(wave_max_i32(hi));
+    wg_id_range(kseg_lo, kseg_hi, sWaveSeg, wave, lane, gseg_lo, gseg_hi);
   }
 
   // with a bias (outside ring steps): the lane's part of sum_i dS_ij for its key, the bias gradient
@@ -596,7 +620,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     if (tid < BQ) {
       sL[slot][tid] = (lok && lreg != -INFINITY) ? -lreg * kLog2e : -INFINITY;
       sDl[slot][tid] = lok ? -dreg : 0.f;
-      if constexpr (HAS_SEG) sSg[slot][tid] = lok ? sreg : 0;
+      if constexpr (HAS_SEG) {
+        static_assert(!HAS_SEG || BQ == 64, "one wave holds a segment tile's ids");
+        const int sid = lok ? sreg : 0;
+        sSg[slot][tid] = sid;
+        const int lo = wave_min_i32(lok ? sid : INT32_MAX);
+        const int hi = wave_max_i32(lok ? sid : INT32_MIN);
+        if (tid == 0) {
+          sTileSeg[slot][0] = lo;
+          sTileSeg[slot][1] = hi;
+        }
+      }
     }
   };
   auto issue_qg = [&](int row0, int rend, int slot) {
@@ -679,11 +713,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     const __bf16* Gt = sG[buf];
     const int qpos0 = row0 + pbase;                      // global position of the tile's row 0
     const int nq = (rend - row0) < BQ ? (rend - row0) : BQ;
-    const bool wave_active = wk_ok && !(CAUSAL && qpos0 + nq - 1 < (CBLK ? wq_first : wkey));
+    bool wave_active = wk_ok && !(CAUSAL && qpos0 + nq - 1 < (CBLK ? wq_first : wkey));
+    bool seg_mask = HAS_SEG;   // some pair of the tile may lie in different segments
+    if constexpr (HAS_SEG) {
+      const int tlo = __builtin_amdgcn_readfirstlane(sTileSeg[buf][0]);
+      const int thi = __builtin_amdgcn_readfirstlane(sTileSeg[buf][1]);
+      wave_active = wave_active && tlo <= kseg_hi && thi >= kseg_lo;
+      seg_mask = !(tlo == thi && kseg_lo == kseg_hi && tlo == kseg_lo);
+    }
     if (wave_active) {
       // rows past the rank's end carry -inf in sL, so their P is 0 and only the causal and
       // segment masks need the selects
-      const bool need_mask = HAS_SEG || (CAUSAL && (CBLK ? wq_last : wkey + KW - 1) > qpos0);
+      const bool need_mask = seg_mask || (CAUSAL && (CBLK ? wq_last : wkey + KW - 1) > qpos0);
       int krel[NKB];   // first query row (of the tile) that sees the lane's key, clamped to [0, BQ]
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -706,7 +747,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
             nl[4 * g4 + i] = x[i];
             dl[4 * g4 + i] = y[i];
           }
-          if constexpr (HAS_SEG) {
+          if (HAS_SEG && need_mask) {
             const int4 z = *reinterpret_cast<const int4*>(&sSg[buf][base]);
             qs[4 * g4 + 0] = z.x;
             qs[4 * g4 + 1] = z.y;

@@ -293,11 +293,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     const __bf16* Kt = sK[buf];
     const __bf16* Vt = sV[buf];
     bool wave_active = wlast >= 0 && !(CAUSAL && key0 > (CBLK ? wlim_last : wpos + wlast));
+    bool seg_mask = HAS_SEG;   // some pair of the tile may lie in different segments
     if constexpr (HAS_SEG) {
       // no key of the tile shares a segment with the wave's queries: every pair is masked
       const int klo = __builtin_amdgcn_readfirstlane(sSegRange[buf][0]);
       const int khi = __builtin_amdgcn_readfirstlane(sSegRange[buf][1]);
       wave_active = wave_active && klo <= qseg_hi && khi >= qseg_lo;
+      // every key and every query of the wave in one segment: the segment mask selects nothing
+      seg_mask = !(klo == khi && qseg_lo == qseg_hi && klo == qseg_lo);
     }
     if (wave_active) {
       // ---- S^T = K . Q^T : rows = 64 keys (two 32-row blocks), columns = the wave's queries
@@ -317,9 +320,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         }
       }
 
-      const bool need_mask = HAS_SEG || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > (CBLK ? wlim_first : wpos));
+      const bool need_mask = seg_mask || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > (CBLK ? wlim_first : wpos));
       int kseg[2][16];
-      if constexpr (HAS_SEG) {
+      if (HAS_SEG && need_mask) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
