@@ -352,12 +352,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         // masked scores become -inf (then P = 0) in a pass of their own, so that tiles
         // without masks run the loop below with no selects
         if (need_mask) {
+          // key rows are kr0(v) + 4 * hh with kr0 a constant of v: compare against the shifted limit
+          const int klim4 = klim - 4 * hh;
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const int kr = mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-              bool vis = kr <= klim;
+              bool vis = mb * 32 + 8 * (v >> 2) + (v & 3) <= klim4;
               if constexpr (HAS_SEG) vis = vis && kseg[mb][v] == qseg[nb];
               S[mb][nb][v] = vis ? S[mb][nb][v] : -INFINITY;
             }
@@ -780,15 +781,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         // without masks run the loop below with no selects
         if (need_mask) {
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb) {
+            // query rows are qr0(v) + 4 * hh with qr0 a constant of v: compare against the shifted
+            // first row, so the row numbers never occupy registers
+            const int krel4 = krel[kb] - 4 * hh;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const int qr = qb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
               bool vis = true;
-              if constexpr (CAUSAL) vis = krel[kb] <= qr;
+              if constexpr (CAUSAL) vis = krel4 <= qb * 32 + 8 * (v >> 2) + (v & 3);
               if constexpr (HAS_SEG) vis = vis && ksg[kb] == qs[v];
               S[kb][v] = vis ? S[kb][v] : -INFINITY;
             }
+          }
         }
         bf16x8 Pb[NKB][2], Sb[NKB][2];
 #pragma unroll

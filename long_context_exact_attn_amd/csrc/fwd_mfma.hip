@@ -356,12 +356,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
             const int rel = CBLK ? qlim[nb] - key0 : wpos - key0 + nb * 32 + l32;
             klim = rel < klim ? (rel < -1 ? -1 : rel) : klim;
           }
+          // the lane's key rows are kr0(v) + 4 * hh with kr0 a constant of v: compare kr0
+          // against the shifted limit, so the row numbers never occupy registers
+          const int klim4 = klim - 4 * hh;
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const int kr = mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-              bool vis = kr <= klim;
+              bool vis = mb * 32 + 8 * (v >> 2) + (v & 3) <= klim4;
               if constexpr (HAS_SEG) vis = vis && kseg[mb][v] == qseg[nb];
               S[mb][nb][v] = vis ? S[mb][nb][v] : -INFINITY;
             }
