@@ -171,15 +171,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   // instead (finite values that the masks give zero weight).
   const int64_t kv_bh = (static_cast<int64_t>(b) * p.Lk * p.H + h) * D;   // (b, key 0, h)
   const int64_t kstride = static_cast<int64_t>(p.H) * D;                 // elements per key
-  int grow_[NSEG], goff[NSEG], goff0[NSEG];
+  // per-lane byte offsets from the tile's first row: goff for the lane's own row, goff0 for row 0
+  int grow_[NSEG];
+  unsigned goff[NSEG], goff0[NSEG];
 #pragma unroll
   for (int j = 0; j < NSEG; ++j) {
     const int byte = (wave * NSEG + j) * 1024 + lane * 16;
     const int row = byte / (2 * D);
     const int chunk = ((byte % (2 * D)) >> 4) ^ swz_key<D>(row);
     grow_[j] = row;
-    goff[j] = row * static_cast<int>(kstride) + chunk * 8;   // < 64 * H * D, checked on the host
-    goff0[j] = chunk * 8;
+    // < 2 * 128 * H * D bytes, which the host keeps below 2^32
+    goff[j] = 2u * static_cast<unsigned>(row * static_cast<int>(kstride) + chunk * 8);
+    goff0[j] = 2u * static_cast<unsigned>(chunk * 8);
   }
   // bias / segment ids of the tile (plain loads; the raw values are kept until store_small,
   // before the barrier, so that the wait for these loads lands there)
@@ -215,13 +218,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   auto issue_kv = [&](int key0, int kend, int slot) {
     const __bf16* kb = kp + kv_bh + static_cast<int64_t>(key0) * kstride;
     const __bf16* vb = vp + kv_bh + static_cast<int64_t>(key0) * kstride;
-    const bool full = key0 + BK <= kend;
-    const int nvalid = kend - key0;
+    if (key0 + BK <= kend) {
 #pragma unroll
-    for (int j = 0; j < NSEG; ++j) {
-      const int off = (full || grow_[j] < nvalid) ? goff[j] : goff0[j];
-      dma16(kb + off, &sK[slot][(wave * NSEG + j) * 512]);
-      dma16(vb + off, &sV[slot][(wave * NSEG + j) * 512]);
+      for (int j = 0; j < NSEG; ++j) {
+        dma16_sb(kb, goff[j], &sK[slot][(wave * NSEG + j) * 512]);
+        dma16_sb(vb, goff[j], &sV[slot][(wave * NSEG + j) * 512]);
+      }
+    } else {
+      const int nvalid = kend - key0;
+#pragma unroll
+      for (int j = 0; j < NSEG; ++j) {
+        const unsigned off = grow_[j] < nvalid ? goff[j] : goff0[j];
+        dma16_sb(kb, off, &sK[slot][(wave * NSEG + j) * 512]);
+        dma16_sb(vb, off, &sV[slot][(wave * NSEG + j) * 512]);
+      }
     }
   };
 

@@ -108,6 +108,22 @@ __device__ __forceinline__ void dma16(const void* g, __bf16* lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(dst), "v"(g) : "memory", "m0");
 }
 
+// The same copy from a wave-uniform base address held in SGPRs plus a 32-bit per-lane byte
+// offset (the instruction's saddr form): the per-lane part stays loop-invariant, so a tile's
+// copies need no 64-bit address arithmetic on the vector unit.
+// (base must be wave-uniform; the compiler cannot always prove it, so it is read from lane 0,
+// which folds away where the value already sits in SGPRs)
+__device__ __forceinline__ void dma16_sb(const void* base, unsigned off_bytes, __bf16* lds) {
+  const unsigned dst = static_cast<unsigned>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) void*)lds));
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a >> 32));
+  const unsigned long long sbase = (static_cast<unsigned long long>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(dst), "v"(off_bytes), "s"(sbase)
+               : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding).
 #define RA_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
 

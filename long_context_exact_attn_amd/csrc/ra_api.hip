@@ -77,7 +77,8 @@ int check_shape(const ra_shape* s, int32_t n_ring, Checked* c) {
   if (s->kv_len >= kMaxPos || s->q_len >= kMaxPos)
     return fail(RA_ERR_SHAPE, "sequence lengths must be below 2^30 (q_len %lld, kv_len %lld)", (long long)s->q_len,
                 (long long)s->kv_len);
-  // the kernels address the rows of one tile (at most 128 rows) with 32-bit offsets
+  // the kernels address the rows of one tile (at most 128 rows) with 32-bit element offsets and
+  // 32-bit unsigned byte offsets
   if (static_cast<int64_t>(s->heads) * s->head_dim * 128 >= (int64_t(1) << 31))
     return fail(RA_ERR_SHAPE, "heads*head_dim too large (%lld)", (long long)s->heads * s->head_dim);
   ra::Params& p = c->p;
