@@ -22,6 +22,8 @@
 //     S^T = K . Q^T,  dP^T = V . dO^T,  dS^T as above,  dQ^T += K^T . dS^T
 //   with the same folding: Q held pre-multiplied by scale * log2e, accumulators started at
 //   bias - lse * log2e and -Delta.
+#include <type_traits>
+
 #include "mfma_util.cuh"
 
 
@@ -269,10 +271,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) qlim[nb] = causal_last_key(wpos + nb * 32 + l32, coff, p.causal);
   }
-  int slot = 0;
-  while (tok[0]) {
+  // one step of the walk per ring stage, unrolled over the stages so that each stage's LDS
+  // addresses are compile-time offsets (no per-tile address arithmetic on the vector unit)
+  auto step = [&](auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
     const int key0 = tk0[0], kend = tke[0];
-    const int ahead = slot + NS - 1 >= NS ? slot - 1 : slot + NS - 1;   // (slot + NS - 1) % NS
+    constexpr int ahead = (slot + NS - 1) % NS;
     const bool issue = tok[NS - 1];
     if (issue) {
       load_small(tk0[NS - 1], tke[NS - 1]);
@@ -402,7 +406,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       RA_WAIT_VMCNT(0);
     }
     __syncthreads();
-    slot = slot + 1 == NS ? 0 : slot + 1;
 #pragma unroll
     for (int i = 0; i + 1 < NS; ++i) {
       tok[i] = tok[i + 1];
@@ -412,6 +415,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     tok[NS - 1] = next_tile();
     tk0[NS - 1] = walk.key0;
     tke[NS - 1] = walk.kend;
+  };
+  static_assert(NS == 2 || NS == 3, "the walk is unrolled over two or three stages");
+  while (tok[0]) {
+    step(std::integral_constant<int, 0>{});
+    if (!tok[0]) break;
+    step(std::integral_constant<int, 1>{});
+    if constexpr (NS == 3) {
+      if (!tok[0]) break;
+      step(std::integral_constant<int, 2>{});
+    }
   }
 
   if constexpr (STEP) {
