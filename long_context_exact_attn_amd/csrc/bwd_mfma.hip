@@ -271,12 +271,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) qlim[nb] = causal_last_key(wpos + nb * 32 + l32, coff, p.causal);
   }
-  // one step of the walk per ring stage, unrolled over the stages so that each stage's LDS
-  // addresses are compile-time offsets (no per-tile address arithmetic on the vector unit)
-  auto step = [&](auto slot_c) {
-    constexpr int slot = decltype(slot_c)::value;
+  int slot = 0;
+  while (tok[0]) {
     const int key0 = tk0[0], kend = tke[0];
-    constexpr int ahead = (slot + NS - 1) % NS;
+    const int ahead = slot + NS - 1 >= NS ? slot - 1 : slot + NS - 1;   // (slot + NS - 1) % NS
     const bool issue = tok[NS - 1];
     if (issue) {
       load_small(tk0[NS - 1], tke[NS - 1]);
@@ -406,6 +404,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       RA_WAIT_VMCNT(0);
     }
     __syncthreads();
+    slot = slot + 1 == NS ? 0 : slot + 1;
 #pragma unroll
     for (int i = 0; i + 1 < NS; ++i) {
       tok[i] = tok[i + 1];
@@ -415,16 +414,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     tok[NS - 1] = next_tile();
     tk0[NS - 1] = walk.key0;
     tke[NS - 1] = walk.kend;
-  };
-  static_assert(NS == 2 || NS == 3, "the walk is unrolled over two or three stages");
-  while (tok[0]) {
-    step(std::integral_constant<int, 0>{});
-    if (!tok[0]) break;
-    step(std::integral_constant<int, 1>{});
-    if constexpr (NS == 3) {
-      if (!tok[0]) break;
-      step(std::integral_constant<int, 2>{});
-    }
   }
 
   if constexpr (STEP) {
@@ -605,19 +594,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   // the tile go through registers.
   const int64_t qstride = static_cast<int64_t>(p.H) * D;
   const int64_t q_bh = (static_cast<int64_t>(b) * p.Lq * p.H + h) * D;   // (b, row 0, h)
-  // per-lane byte offsets from the tile's first row: goff for the lane's own row, goff0 for row 0
-  int grow_[NSEG];
-  unsigned goff[NSEG], goff0[NSEG];
+  int grow_[NSEG], goff[NSEG], goff0[NSEG];
 #pragma unroll
   for (int jj = 0; jj < NSEG; ++jj) {
     const int byte = (wave * NSEG + jj) * 1024 + lane * 16;
     const int row = byte / (2 * D);
     const int chunk = ((byte % (2 * D)) >> 4) ^ swz_key<D>(row);
     grow_[jj] = row;
-    // < 2 * 128 * H * D bytes, which the host keeps below 2^32
-    goff[jj] = 2u * static_cast<unsigned>(row * static_cast<int>(qstride) + chunk * 8);
-    goff0[jj] = 2u * static_cast<unsigned>(chunk * 8);
+    goff[jj] = row * static_cast<int>(qstride) + chunk * 8;   // < 128 * H * D, checked on the host
+    goff0[jj] = chunk * 8;
   }
+  // For head_dim 64 without bias or segment ids the copies take the tile's base from SGPRs and a
+  // 32-bit per-lane byte offset (2 goff < 2^32, which the host ensures) as their only per-lane
+  // operand; the other variants form 64-bit addresses, since the SGPR bases push them into spills.
+  constexpr bool kUniformCopies = D == 64 && !HAS_BIAS && !HAS_SEG;
   // (raw values are kept until the store, so that the wait for these loads lands there and
   // not right after them)
   float lreg = 0.f, dreg = 0.f;
@@ -654,19 +644,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   auto issue_qg = [&](int row0, int rend, int slot) {
     const __bf16* qb_ = qp + q_bh + static_cast<int64_t>(row0) * qstride;
     const __bf16* gb_ = gp + q_bh + static_cast<int64_t>(row0) * qstride;
-    if (row0 + BQ <= rend) {
-#pragma unroll
-      for (int jj = 0; jj < NSEG; ++jj) {
-        dma16_sb(qb_, goff[jj], &sQ[slot][(wave * NSEG + jj) * 512]);
-        dma16_sb(gb_, goff[jj], &sG[slot][(wave * NSEG + jj) * 512]);
-      }
-    } else {
+    if constexpr (kUniformCopies) {
+      const bool full = row0 + BQ <= rend;
       const int nvalid = rend - row0;
 #pragma unroll
       for (int jj = 0; jj < NSEG; ++jj) {
-        const unsigned off = grow_[jj] < nvalid ? goff[jj] : goff0[jj];
+        const unsigned off = 2u * static_cast<unsigned>(full ? goff[jj] : (grow_[jj] < nvalid ? goff[jj] : goff0[jj]));
         dma16_sb(qb_, off, &sQ[slot][(wave * NSEG + jj) * 512]);
         dma16_sb(gb_, off, &sG[slot][(wave * NSEG + jj) * 512]);
+      }
+    } else {
+      const bool full = row0 + BQ <= rend;
+      const int nvalid = rend - row0;
+#pragma unroll
+      for (int jj = 0; jj < NSEG; ++jj) {
+        const int off = (full || grow_[jj] < nvalid) ? goff[jj] : goff0[jj];
+        dma16(qb_ + off, &sQ[slot][(wave * NSEG + jj) * 512]);
+        dma16(gb_ + off, &sG[slot][(wave * NSEG + jj) * 512]);
       }
     }
   };

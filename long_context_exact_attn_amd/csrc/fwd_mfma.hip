@@ -173,19 +173,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   // instead (finite values that the masks give zero weight).
   const int64_t kv_bh = (static_cast<int64_t>(b) * p.Lk * p.H + h) * D;   // (b, key 0, h)
   const int64_t kstride = static_cast<int64_t>(p.H) * D;                 // elements per key
-  // per-lane byte offsets from the tile's first row: goff for the lane's own row, goff0 for row 0
-  int grow_[NSEG];
-  unsigned goff[NSEG], goff0[NSEG];
+  int grow_[NSEG], goff[NSEG], goff0[NSEG];
 #pragma unroll
   for (int j = 0; j < NSEG; ++j) {
     const int byte = (wave * NSEG + j) * 1024 + lane * 16;
     const int row = byte / (2 * D);
     const int chunk = ((byte % (2 * D)) >> 4) ^ swz_key<D>(row);
     grow_[j] = row;
-    // < 2 * 128 * H * D bytes, which the host keeps below 2^32
-    goff[j] = 2u * static_cast<unsigned>(row * static_cast<int>(kstride) + chunk * 8);
-    goff0[j] = 2u * static_cast<unsigned>(chunk * 8);
+    goff[j] = row * static_cast<int>(kstride) + chunk * 8;   // < 64 * H * D, checked on the host
+    goff0[j] = chunk * 8;
   }
+  // For head_dim 64 without bias or segment ids the copies take the tile's base from SGPRs and a
+  // 32-bit per-lane byte offset (2 goff < 2^32, which the host ensures) as their only per-lane
+  // operand; the other variants form 64-bit addresses, since the SGPR bases push them into spills.
+  constexpr bool kUniformCopies = D == 64 && !HAS_BIAS && !HAS_SEG;
   // bias / segment ids of the tile (plain loads; the raw values are kept until store_small,
   // before the barrier, so that the wait for these loads lands there)
   float breg = 0.f;
@@ -220,19 +221,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   auto issue_kv = [&](int key0, int kend, int slot) {
     const __bf16* kb = kp + kv_bh + static_cast<int64_t>(key0) * kstride;
     const __bf16* vb = vp + kv_bh + static_cast<int64_t>(key0) * kstride;
-    if (key0 + BK <= kend) {
-#pragma unroll
-      for (int j = 0; j < NSEG; ++j) {
-        dma16_sb(kb, goff[j], &sK[slot][(wave * NSEG + j) * 512]);
-        dma16_sb(vb, goff[j], &sV[slot][(wave * NSEG + j) * 512]);
-      }
-    } else {
+    if constexpr (kUniformCopies) {
+      const bool full = key0 + BK <= kend;
       const int nvalid = kend - key0;
 #pragma unroll
       for (int j = 0; j < NSEG; ++j) {
-        const unsigned off = grow_[j] < nvalid ? goff[j] : goff0[j];
+        const unsigned off = 2u * static_cast<unsigned>(full ? goff[j] : (grow_[j] < nvalid ? goff[j] : goff0[j]));
         dma16_sb(kb, off, &sK[slot][(wave * NSEG + j) * 512]);
         dma16_sb(vb, off, &sV[slot][(wave * NSEG + j) * 512]);
+      }
+    } else {
+      const bool full = key0 + BK <= kend;
+      const int nvalid = kend - key0;
+#pragma unroll
+      for (int j = 0; j < NSEG; ++j) {
+        const int off = (full || grow_[j] < nvalid) ? goff[j] : goff0[j];
+        dma16(kb + off, &sK[slot][(wave * NSEG + j) * 512]);
+        dma16(vb + off, &sV[slot][(wave * NSEG + j) * 512]);
       }
     }
   };
@@ -292,12 +297,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) qlim[nb] = causal_last_key(wpos + nb * 32 + l32, coff, p.causal);
   }
-  // one step of the walk per ring stage, unrolled over the stages so that each stage's LDS
-  // addresses are compile-time offsets (no per-tile address arithmetic on the vector unit)
+  // one step of the walk per ring stage.  For head_dim 64 without bias or segment ids the walk
+  // is unrolled over the stages, so that each stage's LDS addresses are compile-time offsets (no
+  // per-tile address arithmetic on the vector unit); the other variants keep a runtime stage,
+  // since the unrolled bodies push them into spills.
+  constexpr bool kUnrollWalk = D == 64 && !HAS_BIAS && !HAS_SEG;
   auto step = [&](auto slot_c) {
-    constexpr int slot = decltype(slot_c)::value;
+    const int slot = slot_c;   // a compile-time constant when the walk is unrolled
     const int key0 = tk0[0], kend = tke[0];
-    constexpr int ahead = (slot + NS - 1) % NS;
+    const int ahead = slot + NS - 1 >= NS ? slot - 1 : slot + NS - 1;   // (slot + NS - 1) % NS
     const bool issue = tok[NS - 1];
     if (issue) {
       load_small(tk0[NS - 1], tke[NS - 1]);   // before the copies: its wait then spares them
@@ -455,14 +463,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     tk0[NS - 1] = walk.key0;
     tke[NS - 1] = walk.kend;
   };
-  static_assert(NS == 2 || NS == 3, "the walk is unrolled over two or three stages");
-  while (tok[0]) {
-    step(std::integral_constant<int, 0>{});
-    if (!tok[0]) break;
-    step(std::integral_constant<int, 1>{});
-    if constexpr (NS == 3) {
+  if constexpr (kUnrollWalk) {
+    static_assert(NS == 2 || NS == 3, "the walk is unrolled over two or three stages");
+    while (tok[0]) {
+      step(std::integral_constant<int, 0>{});
       if (!tok[0]) break;
-      step(std::integral_constant<int, 2>{});
+      step(std::integral_constant<int, 1>{});
+      if constexpr (NS == 3) {
+        if (!tok[0]) break;
+        step(std::integral_constant<int, 2>{});
+      }
+    }
+  } else {
+    int slot = 0;
+    while (tok[0]) {
+      step(slot);
+      slot = slot + 1 == NS ? 0 : slot + 1;
     }
   }
 
