@@ -94,6 +94,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   const __bf16* __restrict__ kp = static_cast<const __bf16*>(p.k);
   const __bf16* __restrict__ vp = static_cast<const __bf16*>(p.v);
 
+  // Without a bias or segment ids the score accumulators start from a held register copy of
+  // -m (the row's reference maximum; 0 while it is -inf) and Q is held pre-multiplied by
+  // c = scale * log2e (rounded to bfloat16), so the matrix unit delivers the exponent
+  // c s - m directly and the vector unit is left with the exponential.  The other variants
+  // have no registers to spare for the held copy: they keep raw Q and form c s - m per score.
+  constexpr bool kFold = !HAS_BIAS && !HAS_SEG;
+  const float c = p.scale * kLog2e;   // raw score -> log2 units
   // ---- the wave's queries, as the B operand of S^T = K . Q^T
   const int64_t wrow0 = qa + wave * QW;                      // first row of the wave inside the block
   const int64_t wpos0 = pos0 + wave * QW;
@@ -107,7 +114,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       bf16x8 x = *reinterpret_cast<const bf16x8*>(src + 16 * kk + 8 * hh);
-      Qf[nb][kk] = ok ? x : bf16x8{};
+      Qf[nb][kk] = !ok ? bf16x8{} : (kFold ? scale_bf16x8(x, c) : x);
     }
   }
   int qseg[NQB];
@@ -131,13 +138,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   int gseg_lo = 0, gseg_hi = 0;
   if constexpr (HAS_SEG) wg_id_range(qseg_lo, qseg_hi, sWaveSeg, wave, lane, gseg_lo, gseg_hi);
 
-  const float c = p.scale * kLog2e;   // raw score -> log2 units
   float m[NQB], lsum[NQB];
+  f32x16 minit[NQB];
   f32x16 O[DB][NQB];
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
     m[nb] = -INFINITY;
     lsum[nb] = 0.f;
+    minit[nb] = f32x16{};
 #pragma unroll
     for (int db = 0; db < DB; ++db) O[db][nb] = f32x16{};
   }
@@ -163,6 +171,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         m[nb] = p.m_state[si];
         lsum[nb] = hh == 0 ? p.l_state[si] : 0.f;
       }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+      const float ms = m[nb] == -INFINITY ? 0.f : -m[nb];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) minit[nb][v] = ms;
     }
   }
 
@@ -326,11 +340,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     }
     if (wave_active) {
       // ---- S^T = K . Q^T : rows = 64 keys (two 32-row blocks), columns = the wave's queries
+      // (kFold: in log2 units, minus the row's reference maximum)
       f32x16 S[2][NQB];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NQB; ++nb) S[mb][nb] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
           const bf16x8 a = lds_read_swz<D>(Kt, mb * 32 + l32, 2 * kk + hh);
 #pragma unroll
           for (int nb = 0; nb < NQB; ++nb)
-            S[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Qf[nb][kk], S[mb][nb], 0, 0, 0);
+            S[mb][nb] = mfma32(a, Qf[nb][kk], kk > 0 ? S[mb][nb] : (kFold ? minit[nb] : f32x16{}));
         }
       }
 
@@ -359,7 +370,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       bf16x8 P[NQB][2][2];   // [query block][key block][16-key step]
 #pragma unroll
       for (int nb = 0; nb < NQB; ++nb) {
-        // logits in log2 units when there is a bias (else raw scores, scaled inside the exp)
+        // logits in log2 units when there is a bias (else, without kFold, raw scores scaled
+        // inside the exponential)
         if constexpr (HAS_BIAS) {
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
@@ -396,20 +408,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 #pragma unroll
           for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[mb][nb][v]);
         mx = pair_max(mx);
-        const float mxs = HAS_BIAS ? mx : mx * c;
+        // the offset already taken off the scores (kFold), and the tile's maximum in absolute terms
+        const float msub0 = (m[nb] == -INFINITY) ? 0.f : m[nb];
+        const float mxa = kFold ? mx + msub0 : (HAS_BIAS ? mx : mx * c);
         // Each row decides for itself whether its maximum grew by more than kTau; the
         // multiply runs only when some row of the wave needs it, with alpha = 1 (exact)
         // for the others, so a row's result never depends on its neighbours' data.
-        const bool grow = mxs > m[nb] + kTau;
+        const bool grow = mxa > m[nb] + kTau;
         if (__ballot(grow) != 0) {
-          const float mnew = grow ? mxs : m[nb];
+          const float mnew = grow ? mxa : m[nb];
           const float alpha = grow ? __builtin_amdgcn_exp2f(m[nb] - mnew) : 1.f;   // m = -inf gives 0
           lsum[nb] *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db) O[db][nb] *= alpha;
           m[nb] = mnew;
+          if constexpr (kFold) {
+            // move the tile's scores and the held offset to the new reference
+            const float shift = grow ? mnew - msub0 : 0.f;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) S[mb][nb][v] -= shift;
+            const float ms = m[nb] == -INFINITY ? 0.f : -m[nb];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) minit[nb][v] = ms;
+          }
         }
-        const float msub = (m[nb] == -INFINITY) ? 0.f : m[nb];
+        const float msub = kFold ? 0.f : ((m[nb] == -INFINITY) ? 0.f : m[nb]);
         float acc[2][2];   // row sum in independent partial sums (no serial dependency chain)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -419,7 +444,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
               const float x = S[mb][nb][8 * st + i];
-              e[i] = HAS_BIAS ? __builtin_amdgcn_exp2f(x - msub) : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -msub));
+              e[i] = kFold      ? __builtin_amdgcn_exp2f(x)
+                     : HAS_BIAS ? __builtin_amdgcn_exp2f(x - msub)
+                                : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -msub));
             }
             P[nb][mb][st] = pack_bf16x8(e);
             acc[mb][st] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
