@@ -26,6 +26,7 @@ namespace {
 
 constexpr int BK = 64;            // keys per K/V tile
 constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
+constexpr float kSumMax = 256.0f; // 2^kTau
 
 // LDS stages of the K/V ring (two: one tile in flight while one is computed; a third
 // stage measured slower at head_dim 64).
@@ -339,119 +340,152 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       seg_mask = !(klo == khi && qseg_lo == qseg_hi && klo == qseg_lo);
     }
     if (wave_active) {
-      // ---- S^T = K . Q^T : rows = 64 keys (two 32-row blocks), columns = the wave's queries
-      // (kFold: in log2 units, minus the row's reference maximum)
-      f32x16 S[2][NQB];
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 a = lds_read_swz<D>(Kt, mb * 32 + l32, 2 * kk + hh);
-#pragma unroll
-          for (int nb = 0; nb < NQB; ++nb)
-            S[mb][nb] = mfma32(a, Qf[nb][kk], kk > 0 ? S[mb][nb] : (kFold ? minit[nb] : f32x16{}));
-        }
-      }
-
       const bool need_mask = seg_mask || (key0 + BK > kend) || (CAUSAL && key0 + BK - 1 > (CBLK ? wlim_first : wpos));
-      int kseg[2][16];
-      if (HAS_SEG && need_mask) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int4 x = *reinterpret_cast<const int4*>(&sSeg[buf][mb * 32 + 8 * g4 + 4 * hh]);
-            kseg[mb][4 * g4 + 0] = x.x;
-            kseg[mb][4 * g4 + 1] = x.y;
-            kseg[mb][4 * g4 + 2] = x.z;
-            kseg[mb][4 * g4 + 3] = x.w;
-          }
-      }
       bf16x8 P[NQB][2][2];   // [query block][key block][16-key step]
+      // kFold: a fast pass first.  It takes the exponentials against the held reference without
+      // forming the row maximum.  If every lane's part of the tile's row sum is at most 2^kTau,
+      // no score exceeds the reference by more than kTau, so the exact pass would find no row to
+      // rescale and compute the very same values.  Otherwise (a row's first visible tile, or a
+      // maximum that grew) the tile is done again by the exact pass: row maximum, rescale of the
+      // rows whose maximum grew by more than kTau, exponentials against the new reference.
+      // The other variants take the exact pass only.
+      bool exact = !kFold;
+      if constexpr (kFold) {
+        bool fresh = false;   // a row with no reference yet
 #pragma unroll
-      for (int nb = 0; nb < NQB; ++nb) {
-        // logits in log2 units when there is a bias (else, without kFold, raw scores scaled
-        // inside the exponential)
-        if constexpr (HAS_BIAS) {
+        for (int nb = 0; nb < NQB; ++nb) fresh = fresh || m[nb] == -INFINITY;
+        exact = __ballot(fresh) != 0;
+      }
+      int zoff = 0;
+      for (;;) {
+        // (a second pass reads the K tile from LDS again: its offset goes through an empty asm
+        // statement, so that the compiler does not hold the first pass's reads in registers)
+        if constexpr (kFold) asm volatile("" : "+s"(zoff));
+        const __bf16* Kp = Kt + zoff;
+        // ---- S^T = K . Q^T : rows = 64 keys (two 32-row blocks), columns = the wave's queries
+        // (kFold: in log2 units, minus the row's reference maximum)
+        f32x16 S[2][NQB];
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
+        for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int kr = mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-              S[mb][nb][v] = __builtin_fmaf(S[mb][nb][v], c, sBias[buf][kr]);
-            }
-        }
-        if (need_mask) {
-          // key kr of the tile is visible iff kr <= klim (causal and ragged end) and, with
-          // segments, its id equals the query's; applied with selects, no branches
-          int klim = (kend - key0 < BK ? kend - key0 : BK) - 1;
-          if constexpr (CAUSAL) {
-            // the query's last visible key, relative to key 0
-            const int rel = CBLK ? qlim[nb] - key0 : wpos - key0 + nb * 32 + l32;
-            klim = rel < klim ? (rel < -1 ? -1 : rel) : klim;
+          for (int mb = 0; mb < 2; ++mb) {
+            const bf16x8 a = lds_read_swz<D>(Kp, mb * 32 + l32, 2 * kk + hh);
+#pragma unroll
+            for (int nb = 0; nb < NQB; ++nb)
+              S[mb][nb] = mfma32(a, Qf[nb][kk], kk > 0 ? S[mb][nb] : (kFold ? minit[nb] : f32x16{}));
           }
-          // the lane's key rows are kr0(v) + 4 * hh with kr0 a constant of v: compare kr0
-          // against the shifted limit, so the row numbers never occupy registers
-          const int klim4 = klim - 4 * hh;
+        }
+        int kseg[2][16];
+        if (HAS_SEG && need_mask) {
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              bool vis = mb * 32 + 8 * (v >> 2) + (v & 3) <= klim4;
-              if constexpr (HAS_SEG) vis = vis && kseg[mb][v] == qseg[nb];
-              S[mb][nb][v] = vis ? S[mb][nb][v] : -INFINITY;
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int4 x = *reinterpret_cast<const int4*>(&sSeg[buf][mb * 32 + 8 * g4 + 4 * hh]);
+              kseg[mb][4 * g4 + 0] = x.x;
+              kseg[mb][4 * g4 + 1] = x.y;
+              kseg[mb][4 * g4 + 2] = x.z;
+              kseg[mb][4 * g4 + 3] = x.w;
             }
         }
-        float mx = -INFINITY;
+        bool ok = true;
+        float part[NQB];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[mb][nb][v]);
-        mx = pair_max(mx);
-        // the offset already taken off the scores (kFold), and the tile's maximum in absolute terms
-        const float msub0 = (m[nb] == -INFINITY) ? 0.f : m[nb];
-        const float mxa = kFold ? mx + msub0 : (HAS_BIAS ? mx : mx * c);
-        // Each row decides for itself whether its maximum grew by more than kTau; the
-        // multiply runs only when some row of the wave needs it, with alpha = 1 (exact)
-        // for the others, so a row's result never depends on its neighbours' data.
-        const bool grow = mxa > m[nb] + kTau;
-        if (__ballot(grow) != 0) {
-          const float mnew = grow ? mxa : m[nb];
-          const float alpha = grow ? __builtin_amdgcn_exp2f(m[nb] - mnew) : 1.f;   // m = -inf gives 0
-          lsum[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) O[db][nb] *= alpha;
-          m[nb] = mnew;
-          if constexpr (kFold) {
-            // move the tile's scores and the held offset to the new reference
-            const float shift = grow ? mnew - msub0 : 0.f;
+        for (int nb = 0; nb < NQB; ++nb) {
+          // logits in log2 units when there is a bias (else, without kFold, raw scores scaled
+          // inside the exponential)
+          if constexpr (HAS_BIAS) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-              for (int v = 0; v < 16; ++v) S[mb][nb][v] -= shift;
-            const float ms = m[nb] == -INFINITY ? 0.f : -m[nb];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) minit[nb][v] = ms;
+              for (int v = 0; v < 16; ++v) {
+                const int kr = mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+                S[mb][nb][v] = __builtin_fmaf(S[mb][nb][v], c, sBias[buf][kr]);
+              }
           }
-        }
-        const float msub = kFold ? 0.f : ((m[nb] == -INFINITY) ? 0.f : m[nb]);
-        float acc[2][2];   // row sum in independent partial sums (no serial dependency chain)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            float e[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float x = S[mb][nb][8 * st + i];
-              e[i] = kFold      ? __builtin_amdgcn_exp2f(x)
-                     : HAS_BIAS ? __builtin_amdgcn_exp2f(x - msub)
-                                : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -msub));
+          if (need_mask) {
+            // key kr of the tile is visible iff kr <= klim (causal and ragged end) and, with
+            // segments, its id equals the query's; applied with selects, no branches
+            int klim = (kend - key0 < BK ? kend - key0 : BK) - 1;
+            if constexpr (CAUSAL) {
+              // the query's last visible key, relative to key 0
+              const int rel = CBLK ? qlim[nb] - key0 : wpos - key0 + nb * 32 + l32;
+              klim = rel < klim ? (rel < -1 ? -1 : rel) : klim;
             }
-            P[nb][mb][st] = pack_bf16x8(e);
-            acc[mb][st] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+            // the lane's key rows are kr0(v) + 4 * hh with kr0 a constant of v: compare kr0
+            // against the shifted limit, so the row numbers never occupy registers
+            const int klim4 = klim - 4 * hh;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                bool vis = mb * 32 + 8 * (v >> 2) + (v & 3) <= klim4;
+                if constexpr (HAS_SEG) vis = vis && kseg[mb][v] == qseg[nb];
+                S[mb][nb][v] = vis ? S[mb][nb][v] : -INFINITY;
+              }
           }
-        lsum[nb] += (acc[0][0] + acc[0][1]) + (acc[1][0] + acc[1][1]);
+          if (exact) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[mb][nb][v]);
+            mx = pair_max(mx);
+            // the offset already taken off the scores (kFold), and the tile's maximum in absolute terms
+            const float msub0 = (m[nb] == -INFINITY) ? 0.f : m[nb];
+            const float mxa = kFold ? mx + msub0 : (HAS_BIAS ? mx : mx * c);
+            // Each row decides for itself whether its maximum grew by more than kTau; the
+            // multiply runs only when some row of the wave needs it, with alpha = 1 (exact)
+            // for the others, so a row's result never depends on its neighbours' data.
+            const bool grow = mxa > m[nb] + kTau;
+            if (__ballot(grow) != 0) {
+              const float mnew = grow ? mxa : m[nb];
+              const float alpha = grow ? __builtin_amdgcn_exp2f(m[nb] - mnew) : 1.f;   // m = -inf gives 0
+              lsum[nb] *= alpha;
+#pragma unroll
+              for (int db = 0; db < DB; ++db) O[db][nb] *= alpha;
+              m[nb] = mnew;
+              if constexpr (kFold) {
+                // move the tile's scores and the held offset to the new reference
+                const float shift = grow ? mnew - msub0 : 0.f;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                  for (int v = 0; v < 16; ++v) S[mb][nb][v] -= shift;
+                const float ms = m[nb] == -INFINITY ? 0.f : -m[nb];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) minit[nb][v] = ms;
+              }
+            }
+          }
+          // exponentials against the reference, packed into P, and the lane's part of the row
+          // sum in independent partial sums (no serial dependency chain)
+          const float msub = kFold ? 0.f : ((m[nb] == -INFINITY) ? 0.f : m[nb]);
+          float acc[2][2];
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+              float e[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const float x = S[mb][nb][8 * st + i];
+                e[i] = kFold      ? __builtin_amdgcn_exp2f(x)
+                       : HAS_BIAS ? __builtin_amdgcn_exp2f(x - msub)
+                                  : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -msub));
+              }
+              P[nb][mb][st] = pack_bf16x8(e);
+              acc[mb][st] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+            }
+          part[nb] = (acc[0][0] + acc[0][1]) + (acc[1][0] + acc[1][1]);
+          ok = ok && part[nb] <= kSumMax;
+        }
+        if (exact || __ballot(!ok) == 0) {
+#pragma unroll
+          for (int nb = 0; nb < NQB; ++nb) lsum[nb] += part[nb];
+          break;
+        }
+        exact = true;
       }
 
       // ---- O^T += V^T . P^T ; V^T operand through transposed LDS reads
