@@ -108,8 +108,11 @@ int ra_blockwise_attn_fwd(const void* q, const void* k, const void* v, const flo
                           const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
                           int32_t causal, void* out, float* lse, const ra_shape* shape, void* stream);
 
-/* Bytes of device workspace ra_blockwise_attn_bwd needs (Delta, float32 [B,H,Lq]), rounded up to 256. */
-size_t ra_blockwise_attn_bwd_workspace_size(const ra_shape* shape);
+/* Bytes of device workspace ra_blockwise_attn_bwd needs for this shape on a ring of n_ring blocks:
+ * Delta, float32 [B,H,Lq], rounded up to 256 (the two backward kernels each own the rows they
+ * write, so no partial sums are needed and the size does not depend on n_ring).  Returns 0 for a
+ * NULL shape, negative sizes or n_ring < 1. */
+size_t ra_blockwise_attn_bwd_workspace_size(const ra_shape* shape, int32_t n_ring);
 
 /*
  * The backward pass plus the gradient of the additive bias (NEXT-4 of the pages' attention_bias,

@@ -166,7 +166,7 @@ int do_bwd_dq(const Checked& c, hipStream_t st) {
 
 extern "C" {
 
-int32_t ra_abi_version(void) { return 1; }
+int32_t ra_abi_version(void) { return 2; }
 
 static int ffn_check(int64_t tokens, int32_t d_model, int32_t d_ff, int64_t chunk) {
   if (tokens < 0 || tokens >= kMaxPos) return fail(RA_ERR_SHAPE, "tokens must be in [0, 2^30) (got %lld)", (long long)tokens);
@@ -259,15 +259,15 @@ int ra_blockwise_attn_fwd(const void* q, const void* k, const void* v, const flo
   return hip_status(ra::launch_fwd_simt(c.p, st), "forward launch");
 }
 
-size_t ra_blockwise_attn_bwd_workspace_size(const ra_shape* shape) {
-  if (!shape || shape->batch < 0 || shape->heads < 0 || shape->q_len < 0) return 0;
+size_t ra_blockwise_attn_bwd_workspace_size(const ra_shape* shape, int32_t n_ring) {
+  if (!shape || shape->batch < 0 || shape->heads < 0 || shape->q_len < 0 || n_ring < 1) return 0;
   const size_t rows = static_cast<size_t>(shape->batch) * shape->heads * shape->q_len;
   return (rows * sizeof(float) + 255) / 256 * 256;
 }
 
 size_t ra_blockwise_attn_bwd_dbias_workspace_size(const ra_shape* shape) {
   if (!shape || shape->batch < 0 || shape->heads < 0 || shape->q_len < 0 || shape->kv_len < 0) return 0;
-  return ra_blockwise_attn_bwd_workspace_size(shape) +
+  return ra_blockwise_attn_bwd_workspace_size(shape, 1) +
          static_cast<size_t>(shape->batch) * shape->heads * shape->kv_len * sizeof(float);
 }
 

@@ -1,5 +1,8 @@
 """Helpers shared by the GPU parity tests: run the HIP path through the C-ABI
 binding, run the oracle on the same (rounded) inputs, and compare."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -58,10 +61,17 @@ def errors(got, ref):
     return max_abs, rel
 
 
+# Rounding a float to bfloat16 (round to nearest even, 8 significant bits) moves it by at most half
+# a unit in the last place, i.e. by at most 2^-8 |x|.  Outputs and gradients are rounded to
+# bfloat16 once, so where |ref| is large that rounding alone can exceed the absolute bound.
+HALF_ULP_BF16 = 2.0 ** -8
+
+
 def assert_close(name, got, ref, dtype, strict=True):
-    """strict: max |got - ref| <= the absolute bound.  Otherwise (small synthetic cases whose
-    values can exceed 4, where bfloat16's own spacing is 2^-7 |x|): elementwise
-    |got - ref| <= bound + 2^-7 |ref|, i.e. the bound plus about one bfloat16 ulp."""
+    """strict: max |got - ref| <= the absolute bound.  Otherwise (small synthetic cases and
+    gradients whose values can exceed 4, where bfloat16's own spacing exceeds the bound):
+    elementwise |got - ref| <= bound + 2^-8 |ref|, the bound plus the half ulp that rounding
+    the result to bfloat16 may cost.  The relative RMS bound applies in both cases."""
     tol = TOL[dtype]
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -72,7 +82,7 @@ def assert_close(name, got, ref, dtype, strict=True):
     if strict or dtype == "f32":
         assert max_abs <= tol["max_abs"], msg
     else:
-        excess = np.abs(got - ref) - (tol["max_abs"] + 2.0 ** -7 * np.abs(ref))
+        excess = np.abs(got - ref) - (tol["max_abs"] + HALF_ULP_BF16 * np.abs(ref))
         assert excess.size == 0 or excess.max() <= 0, msg + f" (worst excess {excess.max():.3e})"
     if tol["rel_rms"] is not None:
         assert rel <= tol["rel_rms"], msg
@@ -102,3 +112,58 @@ def sample_rows(w, n, seed=0):
 
 def make(w, device):
     return W.make(w, device=device)
+
+
+# ------------------------------------------------------------------ the oracle over row blocks
+def workers():
+    """Threads for the oracle: the host's cores, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _split(n, parts):
+    step = max(1, -(-n // parts))
+    return [(i, min(n, i + step)) for i in range(0, n, step)]
+
+
+def _pool_map(fn, items, nthreads):
+    """fn over items in threads, each with a one-thread BLAS (numpy releases the GIL in its
+    loops, so the row blocks run in parallel)."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        with ThreadPoolExecutor(nthreads) as ex:
+            return list(ex.map(fn, items))
+
+
+def oracle_forward_rows(d, q_pos, causal, nthreads=None):
+    """oracle.forward over blocks of query rows in threads; same result as one call."""
+    import oracle
+    nthreads = nthreads or workers()
+    nq = d["q"].shape[1]
+
+    def one(r):
+        i0, i1 = r
+        return oracle.forward(d["q"][:, i0:i1], d["k"], d["v"], q_pos=q_pos[i0:i1], causal=causal, bias=d["bias"],
+                              segment_ids=d["segment_ids"])
+    parts = _pool_map(one, _split(nq, 4 * nthreads), nthreads)
+    return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=2)
+
+
+def oracle_backward_rows(d, q_pos, causal, nthreads=None):
+    """oracle.backward over blocks of query rows in threads: dq by rows, and dk / dv as the sum of
+    every block's contributions (the oracle returns a row subset's contributions)."""
+    import oracle
+    nthreads = nthreads or workers()
+    nq = d["q"].shape[1]
+
+    def one(r):
+        i0, i1 = r
+        return oracle.backward(d["q"][:, i0:i1], d["k"], d["v"], d["dout"][:, i0:i1], q_pos=q_pos[i0:i1],
+                               causal=causal, bias=d["bias"], segment_ids=d["segment_ids"])
+    parts = _pool_map(one, _split(nq, nthreads), nthreads)
+    dq = np.concatenate([p[0] for p in parts], axis=1)
+    dk = parts[0][1]
+    dv = parts[0][2]
+    for p in parts[1:]:
+        dk += p[1]
+        dv += p[2]
+    return dq, dk, dv

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
     assert "ra_blockwise_attn_fwd" in names and "ra_blockwise_attn_bwd" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.ra_abi_version() == 1
+    assert lib.ra_abi_version() == 2
 
 
 def test_shape_struct_layout():
@@ -49,9 +49,12 @@ def test_shape_struct_layout():
 def test_workspace_size():
     lib = _lib()
     s = api.Shape(2, 3, 64, -1, 1000, 1000, 0, 0.0, api.RA_BF16)
-    assert lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(s)) == (2 * 3 * 1000 * 4 + 255) // 256 * 256
+    for n_ring in (1, 4, 1000):
+        assert lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(s), n_ring) == (2 * 3 * 1000 * 4 + 255) // 256 * 256
+    assert lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(s), 0) == 0
+    assert lib.ra_blockwise_attn_bwd_workspace_size(None, 1) == 0
     s = api.Shape(0, 3, 64, -1, 0, 0, 0, 0.0, api.RA_BF16)
-    assert lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(s)) == 0
+    assert lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(s), 1) == 0
 
 
 def _gpu_visible():
@@ -226,7 +229,7 @@ def test_dbias_validation():
     lib = _lib()
     s = api.Shape(1, 2, 64, -1, 1024, 1024, 100, 0.0, api.RA_BF16)
     need = lib.ra_blockwise_attn_bwd_dbias_workspace_size(ctypes.byref(s))
-    assert need == lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(s)) + 1 * 2 * 1024 * 4
+    assert need == lib.ra_blockwise_attn_bwd_workspace_size(ctypes.byref(s), 1) + 1 * 2 * 1024 * 4
 
     def call(shape, bias=FAKE, dbias=FAKE, ws=None, ws_bytes=0, dv=None):
         return lib.ra_blockwise_attn_bwd_dbias(FAKE, FAKE, FAKE, bias, None, 4, 256, 256, 1, FAKE, FAKE, FAKE, FAKE,

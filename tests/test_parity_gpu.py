@@ -37,9 +37,15 @@ def test_tiny_f32_full(gpu):
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
-def test_causal_32k_sampled_rows(gpu):
+def test_causal_32k_full(gpu):
+    # every row of every head against the oracle (row blocks in threads)
     w = W.WORKLOADS["causal-32k"]
-    _check_forward(w, gpu, rows=P.sample_rows(w, 512, seed=1))
+    t = P.make(w, gpu)
+    out, lse = P.gpu_forward(w, t)
+    torch.cuda.synchronize()
+    ref_o, ref_l = P.oracle_forward_rows(P.oracle_inputs(t), w.q_positions(), w.causal)
+    P.assert_close(f"{w.name} out", P.np64(out), ref_o, w.dtype)
+    P.assert_lse(lse.cpu().numpy().astype(np.float64), ref_l, w.dtype)
 
 
 def test_share_1m_rank7_sampled_rows(gpu):
@@ -75,19 +81,84 @@ def test_packed_docs_64k_sampled_rows(gpu):
     _check_forward(w, gpu, rows=P.sample_rows(w, 192, seed=3), heads=slice(0, 32, 7))
 
 
-def test_train_32k_one_head_full_backward(gpu):
+def test_train_32k_full_backward_four_heads(gpu):
+    # dQ, dK, dV of heads 0, 5, 10 and 15 element by element; invariants on every head
     w = W.WORKLOADS["train-32k"]
     t = P.make(w, gpu)
     out, lse = P.gpu_forward(w, t)
     dq, dk, dv = P.gpu_backward(w, t, out, lse)
     torch.cuda.synchronize()
-    h = 3
+    for h in (0, 5, 10, 15):
+        d = P.oracle_inputs(t, heads=slice(h, h + 1))
+        rdq, rdk, rdv = P.oracle_backward_rows(d, w.q_positions(), w.causal)
+        for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            P.assert_close(f"{w.name} {name}[h={h}]", P.np64(g[:, :, h:h + 1]), r, "bf16", strict=False)
+    # invariants on every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i
+    sdk = dk.float().sum(dim=1)
+    sdv, sdo = dv.float().sum(dim=1), t["dout"].float().sum(dim=1)
+    scale_k = dk.float().abs().sum(dim=1)
+    assert torch.all(sdk.abs() <= 2e-2 * scale_k + 1e-3), float((sdk.abs() / scale_k).max())
+    assert torch.allclose(sdv, sdo, rtol=2e-2, atol=2e-1), float((sdv - sdo).abs().max())
+
+
+def test_share_1m_keys_full_head_gradients(gpu):
+    # One rank's launch whose K/V spans all 1,048,576 keys: ring rank 255 of 256 blocks of 4096
+    # tokens, 16 heads, causal.  Head 9's dQ (all 4096 rows) and dK, dV (all 1,048,576 keys, so
+    # every ring block's first and last key, and the top blocks whose byte offsets pass 2^31) are
+    # compared element by element with the oracle, which forms P, lse and Delta itself.
+    w = W.replace(W.WORKLOADS["share-1m-r7"], name="share-1m-keys-r255", n_ring=256, ring_rank=255,
+                  backward=True)
+    t = P.make(w, gpu)
+    out, lse = P.gpu_forward(w, t)
+    dq, dk, dv = P.gpu_backward(w, t, out, lse)
+    torch.cuda.synchronize()
+    h = 9
     d = P.oracle_inputs(t, heads=slice(h, h + 1))
-    import oracle
-    rdq, rdk, rdv, _ = oracle.backward(d["q"], d["k"], d["v"], d["dout"], q_pos=w.q_positions(), causal=True)
+    rdq, rdk, rdv = P.oracle_backward_rows(d, w.q_positions(), w.causal)
     for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
         P.assert_close(f"{w.name} {name}[h={h}]", P.np64(g[:, :, h:h + 1]), r, "bf16")
-    # invariants on every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i
+    # the last ring block's keys: the causal diagonal, partly visible
+    lb = w.block_len
+    P.assert_close(f"{w.name} dk[h={h}] last block", P.np64(dk[:, -lb:, h:h + 1]), rdk[:, -lb:], "bf16")
+
+
+def test_packed_docs_64k_backward(gpu):
+    # The packed-document workload's backward in the launch bench-style runs use: dQ on sampled rows
+    # of three heads; and, for the two shortest documents of each batch row in two heads, dQ of all
+    # their rows and dK, dV of all their keys (a key is seen only by its own document's queries, so
+    # the oracle over that document's rows gives the whole gradient of its keys).
+    w = W.replace(W.WORKLOADS["packed-docs-64k"], backward=True)
+    t = P.make(w, gpu)
+    out, lse = P.gpu_forward(w, t)
+    dq, dk, dv = P.gpu_backward(w, t, out, lse)
+    torch.cuda.synchronize()
+    import oracle
+    rows = P.sample_rows(w, 64, seed=6)
+    heads = (0, 17, 31)
+    for h in heads:
+        d = P.oracle_inputs(t, heads=slice(h, h + 1), rows=rows)
+        rdq, _, _, _ = oracle.backward(d["q"], d["k"], d["v"], d["dout"], q_pos=w.q_positions()[rows],
+                                       causal=w.causal, bias=d["bias"], segment_ids=d["segment_ids"])
+        P.assert_close(f"{w.name} dq[h={h}] sampled", P.np64(dq[:, rows, h:h + 1]), rdq, "bf16", strict=False)
+    seg = t["segment_ids"].cpu().numpy()
+    for b in range(w.batch):
+        ids, starts, counts = np.unique(seg[b], return_index=True, return_counts=True)
+        for doc in ids[np.argsort(counts, kind="stable")[:2]]:
+            sel = np.nonzero(seg[b] == doc)[0]
+            lo, hi = int(sel[0]), int(sel[-1]) + 1
+            for h in (5, 26):
+                tb = {k_: (None if v_ is None else v_[b:b + 1]) for k_, v_ in t.items() if k_ != "bias"}
+                tb["bias"] = t["bias"]
+                d = P.oracle_inputs(tb, heads=slice(h, h + 1), rows=np.arange(lo, hi))
+                rdq, rdk, rdv, _ = oracle.backward(d["q"], d["k"], d["v"], d["dout"], q_pos=np.arange(lo, hi),
+                                                   causal=w.causal, bias=d["bias"], segment_ids=d["segment_ids"])
+                tag = f"{w.name} b={b} doc={doc} [{lo},{hi}) h={h}"
+                P.assert_close(f"{tag} dq", P.np64(dq[b:b + 1, lo:hi, h:h + 1]), rdq, "bf16", strict=False)
+                P.assert_close(f"{tag} dk", P.np64(dk[b:b + 1, lo:hi, h:h + 1]), rdk[:, lo:hi], "bf16",
+                               strict=False)
+                P.assert_close(f"{tag} dv", P.np64(dv[b:b + 1, lo:hi, h:h + 1]), rdv[:, lo:hi], "bf16",
+                               strict=False)
+    # sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i on every (batch, head)
     sdk = dk.float().sum(dim=1)
     sdv, sdo = dv.float().sum(dim=1), t["dout"].float().sum(dim=1)
     scale_k = dk.float().abs().sum(dim=1)
