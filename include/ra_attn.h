@@ -146,6 +146,30 @@ int ra_blockwise_attn_bwd(const void* q, const void* k, const void* v, const flo
                           void* dk, void* dv, void* workspace, size_t workspace_bytes, const ra_shape* shape,
                           void* stream);
 
+/*
+ * The backward pass for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): ra_blockwise_attn_bwd with no workspace argument.  Delta
+ * goes to a 16 MiB array in the library's static device memory, one per GPU, held until the process
+ * ends; the call itself allocates nothing and calls no allocating routine.  Limit: batch * heads *
+ * q_len <= 4,194,304 (ra_blockwise_attn_bwd_noalloc_max_workspace() bytes of Delta), else
+ * RA_ERR_WORKSPACE and nothing is launched.  Results are those of ra_blockwise_attn_bwd, bit for bit.
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one GPU (other streams or
+ * threads) race and must be serialised by the caller.  Errors: as ra_blockwise_attn_bwd, whose
+ * message ra_last_error() holds; errors of this wrapper itself (shape NULL, size over the limit,
+ * no current device) are described by ra_noalloc_last_error().
+ */
+int ra_blockwise_attn_bwd_noalloc(const void* q, const void* k, const void* v, const float* bias,
+                                  const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
+                                  int32_t causal, const void* out, const float* lse, const void* dout, void* dq,
+                                  void* dk, void* dv, const ra_shape* shape, void* stream);
+
+/* Bytes of the static scratch array ra_blockwise_attn_bwd_noalloc uses (its size limit). */
+size_t ra_blockwise_attn_bwd_noalloc_max_workspace(void);
+
+/* Description of the last error of ra_blockwise_attn_bwd_noalloc's own checks on this thread
+ * ("" when the last call passed them). */
+const char* ra_noalloc_last_error(void);
+
 /* Backward phase 1: delta[b,h,i] = sum_d dout[b,i,h,d] * out[b,i,h,d] (float32 [B,H,Lq]). */
 int ra_blockwise_attn_bwd_preprocess(const void* out, const void* dout, float* delta, const ra_shape* shape,
                                      void* stream);

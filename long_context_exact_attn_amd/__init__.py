@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     attn_merge,
     blockwise_attn_bwd_step,
     blockwise_attn_bwd_dbias,
+    blockwise_attn_bwd_noalloc,
     blockwise_ffn_fwd,
     blockwise_ffn_bwd,
     blockwise_attn_bwd_finalize,

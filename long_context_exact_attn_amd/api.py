@@ -60,6 +60,7 @@ def load_library():
         "ra_blockwise_attn_bwd_finalize": [P, P, P, P, P, P, SH, P],
         "ra_blockwise_attn_bwd_dbias": [P, P, P, P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, P, SZ, SH, P],
         "ra_blockwise_ffn_fwd": [P, P, P, P, P, I64, I32, I32, I64, P, SZ, P],
+        "ra_blockwise_attn_bwd_noalloc": [P, P, P, P, P, I32, I64, I64, I32, P, P, P, P, P, P, SH, P],
         "ra_blockwise_ffn_bwd": [P, P, P, P, P, P, P, P, P, I64, I32, I32, I64, P, SZ, P],
     }
     for name, args in sig.items():
@@ -74,6 +75,10 @@ def load_library():
     lib.ra_blockwise_ffn_workspace_size.restype = SZ
     lib.ra_last_error.argtypes = []
     lib.ra_last_error.restype = ctypes.c_char_p
+    lib.ra_noalloc_last_error.argtypes = []
+    lib.ra_noalloc_last_error.restype = ctypes.c_char_p
+    lib.ra_blockwise_attn_bwd_noalloc_max_workspace.argtypes = []
+    lib.ra_blockwise_attn_bwd_noalloc_max_workspace.restype = SZ
     lib.ra_abi_version.argtypes = []
     lib.ra_abi_version.restype = ctypes.c_int32
     if lib.ra_abi_version() != 2:
@@ -230,6 +235,30 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, bias=None, segment_ids=None, *, 
                                      _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), ctypes.byref(shape),
                                      _stream(q.device)))
+    return dq, dk, dv
+
+
+def blockwise_attn_bwd_noalloc(q, k, v, out, lse, dout, bias=None, segment_ids=None, *, n_ring, q_chunk, k_chunk,
+                               causal, ring_rank=-1, scale=None, dq=None, dk=None, dv=None):
+    """dq, dk, dv = ra_blockwise_attn_bwd_noalloc(...): the backward with Delta in the library's static
+    device scratch (no workspace).  Outputs the caller does not pass are allocated here, by torch; pass
+    dq, dk and dv to allocate nothing."""
+    lib = load_library()
+    _tensors(q, k, v, bias, segment_ids, devices=False)
+    shape = make_shape(q, k, ring_rank=ring_rank, scale=scale, bias=bias)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_grads(q, k, out, lse, dout, dq, dk, dv)
+    _tensors(q, k, v, bias, segment_ids, extra=(("out", out), ("lse", lse), ("dout", dout), ("dq", dq), ("dk", dk),
+                                                ("dv", dv)))
+    rc = lib.ra_blockwise_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(n_ring),
+                                           int(q_chunk), int(k_chunk), _causal(causal), _ptr(out), _ptr(lse),
+                                           _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), ctypes.byref(shape),
+                                           _stream(q.device))
+    if rc != 0:
+        own = lib.ra_noalloc_last_error().decode()
+        raise RAError(rc, own or lib.ra_last_error().decode())
     return dq, dk, dv
 
 

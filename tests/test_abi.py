@@ -265,3 +265,17 @@ def test_ffn_validation():
     assert fwd(T=0) == 0   # nothing to do, nothing launched
     rc = lib.ra_blockwise_ffn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 64, 96, 16, None, 0, None)
     assert rc == -1 and b"dw2" in lib.ra_last_error()
+
+
+def test_noalloc_rejects_sizes_over_its_scratch_on_the_host():
+    # the allocation-free backward refuses a problem whose Delta exceeds its static scratch before it
+    # touches a device (all pointers NULL: nothing could be launched)
+    if _gpu_visible():
+        pytest.skip("host-only check")
+    lib = _lib()
+    assert lib.ra_blockwise_attn_bwd_noalloc_max_workspace() == 16 << 20
+    s = api.Shape(1, 65, 64, -1, 65536, 65536, 0, 0.0, api.RA_BF16)
+    rc = lib.ra_blockwise_attn_bwd_noalloc(*([None] * 5), 1, 1, 1, 1, *([None] * 6), ctypes.byref(s), None)
+    assert rc == api.RA_ERR_WORKSPACE if hasattr(api, "RA_ERR_WORKSPACE") else rc == -4
+    assert b"4,194,304" in lib.ra_noalloc_last_error()
+    assert lib.ra_blockwise_attn_bwd_noalloc(*([None] * 5), 1, 1, 1, 1, *([None] * 6), None, None) == -1
