@@ -78,7 +78,8 @@ def parse():
                     help="time the blockwise SwiGLU feed-forward instead (a sweep line): one device's 131072 tokens, "
                          "d_model 1024, d_ff 2816, chunks of --ffn-chunk tokens, forward + backward")
     ap.add_argument("--ffn-chunk", type=int, default=16384, help="tokens per chunk of the blockwise feed-forward")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="query rows in the oracle's fixed seeded sample (cpu_baseline)")
     ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, run one plain device copy of this many MiB (a known-size kernel "
@@ -86,10 +87,23 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, t, target_s):
-    """The float64 oracle, as it stands, on a bounded sample of the same workload: query rows of one head
-    taken in order from a seeded permutation until about target_s seconds of CPU time, each against its
-    full visible key set, forward + backward.  Returns TFLOP/s over the sample's visible pairs."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(w, t, n_rows):
+    """The float64 oracle, as it stands, on a fixed seeded sample of the same workload: n_rows query rows
+    of head 0 (the first rows of a permutation drawn with seed 5) plus the first and last row of every ring
+    block the queries span, each against its full visible key set, forward + backward.  Returns TFLOP/s
+    over the sample's visible pairs and the time the oracle would take for the whole workload at the
+    sample's rate (pairs of every head and batch row)."""
     import numpy as np
     import oracle
     try:
@@ -104,23 +118,93 @@ def cpu_baseline(w, t, target_s):
     bias = None if t["bias"] is None else f64(t["bias"][h:h + 1])
     seg = None if t["segment_ids"] is None else t["segment_ids"].cpu().numpy()
     qpos_all = w.q_positions()
-    perm = np.random.default_rng(5).permutation(w.q_len)
-    done, pairs, elapsed, batch = 0, 0, 0.0, 8
-    while elapsed < target_s and done < w.q_len:
-        rows = np.sort(perm[done:done + batch])
-        q = f64(t["q"][:, rows][:, :, h:h + 1])
-        g = f64(t["dout"][:, rows][:, :, h:h + 1]) if t.get("dout") is not None else np.ones_like(q)
+    rows = set(np.random.default_rng(5).permutation(w.q_len)[:n_rows].tolist())
+    for start in range(0, w.q_len, w.block_len):
+        rows.update((start, min(w.q_len, start + w.block_len) - 1))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    pairs, elapsed, batch = 0, 0.0, 8
+    for i0 in range(0, len(rows), batch):
+        r = rows[i0:i0 + batch]
+        q = f64(t["q"][:, r][:, :, h:h + 1])
+        g = f64(t["dout"][:, r][:, :, h:h + 1]) if t.get("dout") is not None else np.ones_like(q)
         t0 = time.perf_counter()
-        oracle.forward(q, k, v, q_pos=qpos_all[rows], causal=w.causal, bias=bias, segment_ids=seg)
-        oracle.backward(q, k, v, g, q_pos=qpos_all[rows], causal=w.causal, bias=bias, segment_ids=seg)
+        oracle.forward(q, k, v, q_pos=qpos_all[r], causal=w.causal, bias=bias, segment_ids=seg)
+        oracle.backward(q, k, v, g, q_pos=qpos_all[r], causal=w.causal, bias=bias, segment_ids=seg)
         elapsed += time.perf_counter() - t0
-        pairs += int(oracle.visible_pairs(qpos_all[rows], w.kv_len, w.causal, seg[:, :] if seg is not None else None))
-        done += len(rows)
+        pairs += int(oracle.visible_pairs(qpos_all[r], w.kv_len, w.causal, seg))
+    all_pairs = int(oracle.visible_pairs(qpos_all, w.kv_len, w.causal, seg)) * w.heads * (1 if seg is not None
+                                                                                          else w.batch)
     fl = 14 * w.head_dim * pairs
     return {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} query rows of head 0 (seeded permutation), each against its full visible key set, "
-                      f"float64 forward+backward; {pairs} visible pairs in {elapsed:.1f} s; "
-                      f"host {platform.processor() or platform.machine()}"}
+            "cpu_model": cpu_model(),
+            "full_workload_s_extrapolated": round(elapsed * all_pairs / max(pairs, 1), 1),
+            "sample": f"{len(rows)} query rows of head 0 (the first {n_rows} of a permutation drawn with seed 5, "
+                      f"plus the first and last row of each ring block), each against its full visible key set, "
+                      f"float64 forward+backward; {pairs} visible pairs in {elapsed:.1f} s"}
+
+
+def gpu_clocks():
+    """The GPU's current clocks from amd-smi (a child process): the mean over the XCDs' graphics clocks
+    and the memory clock, in MHz, or None where they cannot be read."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        if r.returncode != 0:
+            return None
+        d = json.loads(r.stdout)
+        if isinstance(d, dict) and "gpu_data" in d:
+            d = d["gpu_data"]
+        d = d[0] if isinstance(d, list) else d
+        clk = d.get("clock", {})
+
+        def val(c):
+            c = c.get("clk") if isinstance(c, dict) else None
+            v = c.get("value") if isinstance(c, dict) else c
+            return float(v) if isinstance(v, (int, float)) else None
+        gfx = [val(c) for k_, c in clk.items() if k_.startswith("gfx")]
+        mem = [val(c) for k_, c in clk.items() if k_.startswith("mem")]
+        gfx = [x for x in gfx if x is not None]
+        mem = [x for x in mem if x is not None]
+        if not gfx:
+            return None
+        return {"gfx_mean": round(sum(gfx) / len(gfx), 1), "gfx_min": min(gfx), "gfx_max": max(gfx),
+                "mem": mem[0] if mem else None}
+    except Exception:  # noqa: BLE001 - clocks are informational
+        return None
+
+
+class ClockSampler:
+    """Reads the clocks just before the timed region, every second or so during it (a thread that starts
+    amd-smi as a child process; the GPU work is not touched) and just after it."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.before, self.after = [], None, None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            c = gpu_clocks()
+            if c:
+                self.samples.append(c["gfx_mean"])
+            self._stop.wait(1.0)
+
+    def start(self):
+        self.before = gpu_clocks()
+        self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join(timeout=30)
+        self.after = gpu_clocks()
+
+    def summary(self):
+        during = sorted(self.samples)
+        return {"before": self.before, "after": self.after,
+                "during_gfx_mean": ({"n": len(during), "min": during[0], "median": during[len(during) // 2],
+                                     "max": during[-1]} if during else None)}
 
 
 def bench_ffn(args):
@@ -289,13 +373,20 @@ def main():
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    clocks = ClockSampler()
+    clocks.start()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clocks.stop()
     per = {n: sum(events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)) / args.steps
            for i, n in enumerate(names)}
+    step_ms = sorted(events[s][0].elapsed_time(events[s][-1]) for s in range(args.steps))
+    median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] +
+                                                                          step_ms[len(step_ms) // 2])
     ms_step = wall * 1e3 / args.steps
 
     segn = None if seg is None else seg.cpu().numpy()
@@ -304,6 +395,18 @@ def main():
     if segn is None:
         pairs *= w.batch
     fl = M.flops(pairs, w.head_dim, w.heads)
+    # MFMA work the kernels execute: every tile a wave computes (masked and padding pairs included) at each
+    # kernel's own tile shape; the dQ kernel's recomputation of S and dP included (dense masks only)
+    ex = {}
+    if segn is None and not args.ring_steps:
+        D_, HB_ = w.head_dim, w.heads * w.batch
+        nqb = 2 if w.head_dim == 64 else 1
+        e_fwd = M.executed_pairs_per_head(q_first, w.q_len, w.kv_len, w.causal, 32 * nqb, 64)
+        e_kv = M.executed_pairs_per_head(q_first, w.q_len, w.kv_len, w.causal,
+                                         128 if (w.head_dim == 64 and w.segments == "none") else 64, 32)
+        e_dq = M.executed_pairs_per_head(q_first, w.q_len, w.kv_len, w.causal, 32, 64)
+        if None not in (e_fwd, e_kv, e_dq):
+            ex = {"fwd": 4 * D_ * e_fwd * HB_, "bwd_dkdv": 8 * D_ * e_kv * HB_, "bwd_dq": 6 * D_ * e_dq * HB_}
     kernel_flops = {"fwd": fl["fwd"], "bwd_dkdv": fl["dkdv"], "bwd_dq": fl["dq"], "bwd_steps": fl["dkdv"] + fl["dq"]}
     total_flops = fl["fwd"] if args.fwd_only else fl["fwd_bwd"]
     value = total_flops / (ms_step * 1e-3) / 1e12
@@ -320,6 +423,15 @@ def main():
     dom = max((n for n in names if n in kernel_flops), key=lambda n: per[n])
     ach = kernel_flops[dom] / (per[dom] * 1e-3) / 1e12
     fwd_tflops = fl["fwd"] / (per["fwd"] * 1e-3) / 1e12
+    if ex:
+        ex_total = ex["fwd"] if args.fwd_only else ex["fwd"] + ex["bwd_dkdv"] + ex["bwd_dq"]
+        executed = {"tflops": round(ex_total / (ms_step * 1e-3) / 1e12, 2),
+                    "flop_per_step": ex_total,
+                    "per_kernel_tflops": {n: round(ex[n] / (per[n] * 1e-3) / 1e12, 2) for n in ex if n in per},
+                    "note": "MFMA work executed: whole wave tiles, the dQ kernel's recomputed S and dP included "
+                            "(18*D per pair for the step, against the 14*D counted in value)"}
+    else:
+        executed = None
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -328,6 +440,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3),
+        "ms_per_step_median": round(median_ms, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -346,13 +459,15 @@ def main():
         "fwd_frac_peak": round(fwd_tflops / M.PEAK_BF16_TFLOPS, 4),
         "tokens_per_s": round(w.batch * w.q_len / (ms_step * 1e-3), 1),
         "visible_pairs": pairs * w.heads,
+        "executed": executed,
+        "clocks_mhz": clocks.summary(),
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": M.PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach / M.PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name, dom)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_rows)
     print(json.dumps(line), flush=True)
 
 

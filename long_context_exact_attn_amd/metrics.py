@@ -43,6 +43,26 @@ def flops(pairs, head_dim, heads, batch_rows=1):
             "dq": 6 * head_dim * n, "fwd_bwd": 14 * head_dim * n}
 
 
+def executed_pairs_per_head(q_first, q_len, kv_len, causal, tile_q, tile_k):
+    """(query, key) pairs inside the tile_q x tile_k tiles a kernel computes for one head and batch
+    row: a tile is computed in full (masked and padding pairs included) when the causal mask leaves
+    any of its pairs visible.  Dense masks only (no segment ids); token-level causal or none."""
+    if q_len <= 0 or kv_len <= 0:
+        return 0
+    if causal is not True and causal not in (1, False, 0, None):
+        return None
+    n_kt = -(-kv_len // tile_k)
+    total = 0
+    for r0 in range(0, q_len, tile_q):
+        if causal in (False, 0, None):
+            kt = n_kt
+        else:
+            last = q_first + min(r0 + tile_q, q_len) - 1   # the tile's last existing query
+            kt = min(n_kt, last // tile_k + 1)
+        total += tile_q * tile_k * kt
+    return total
+
+
 # MI355X published peaks
 PEAK_BF16_TFLOPS = 2500.0     # dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # fp32 vector
