@@ -144,39 +144,40 @@ def cpu_baseline(w, t, n_rows):
 
 
 def gpu_clocks():
-    """The GPU's current clocks from amd-smi (a child process): the mean over the XCDs' graphics clocks
-    and the memory clock, in MHz, or None where they cannot be read."""
-    import subprocess
-    try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
-                           timeout=20)
-        if r.returncode != 0:
-            return None
-        d = json.loads(r.stdout)
-        if isinstance(d, dict) and "gpu_data" in d:
-            d = d["gpu_data"]
-        d = d[0] if isinstance(d, list) else d
-        clk = d.get("clock", {})
+    """The GPU's current clocks, read from the driver's sysfs clock tables (no child process): the mean
+    over the graphics clock domains and the memory clock, in MHz, or None where they cannot be read."""
+    import glob
+    import re
 
-        def val(c):
-            c = c.get("clk") if isinstance(c, dict) else None
-            v = c.get("value") if isinstance(c, dict) else c
-            return float(v) if isinstance(v, (int, float)) else None
-        gfx = [val(c) for k_, c in clk.items() if k_.startswith("gfx")]
-        mem = [val(c) for k_, c in clk.items() if k_.startswith("mem")]
-        gfx = [x for x in gfx if x is not None]
-        mem = [x for x in mem if x is not None]
-        if not gfx:
-            return None
-        return {"gfx_mean": round(sum(gfx) / len(gfx), 1), "gfx_min": min(gfx), "gfx_max": max(gfx),
-                "mem": mem[0] if mem else None}
-    except Exception:  # noqa: BLE001 - clocks are informational
+    def current(path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*mhz", line, re.I)
+                        if m:
+                            return float(m.group(1))
+        except OSError:
+            pass
         return None
+    gfx, mem = [], []
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        g = current(os.path.join(dev, "pp_dpm_sclk"))
+        if g is None:
+            continue
+        gfx.append(g)
+        m = current(os.path.join(dev, "pp_dpm_mclk"))
+        if m is not None:
+            mem.append(m)
+    if not gfx:
+        return None
+    return {"gfx_mean": round(sum(gfx) / len(gfx), 1), "gfx_min": min(gfx), "gfx_max": max(gfx),
+            "mem": mem[0] if mem else None}
 
 
 class ClockSampler:
-    """Reads the clocks just before the timed region, every second or so during it (a thread that starts
-    amd-smi as a child process; the GPU work is not touched) and just after it."""
+    """Reads the clocks just before the timed region, every second or so during it (a thread reading sysfs;
+    the GPU work is not touched) and just after it."""
 
     def __init__(self):
         import threading
@@ -189,7 +190,7 @@ class ClockSampler:
             c = gpu_clocks()
             if c:
                 self.samples.append(c["gfx_mean"])
-            self._stop.wait(1.0)
+            self._stop.wait(0.5)
 
     def start(self):
         self.before = gpu_clocks()
