@@ -120,7 +120,7 @@ size_t ra_blockwise_attn_bwd_workspace_size(const ra_shape* shape, int32_t n_rin
  * key j adds bias[h, j mod bias_len] to every query's score, so
  *   dbias[h, t] = sum over b, i and keys j with j mod bias_len = t of dS_ij   (float32, [H, bias_len])
  * with dS as above (no scale factor).  Arguments as ra_blockwise_attn_bwd, plus dbias (device,
- * 4-byte aligned); bias must be given and the dtype must be RA_BF16.  The workspace must hold
+ * 4-byte aligned); bias must be given (RA_BF16 or RA_F32).  The workspace must hold
  * ra_blockwise_attn_bwd_dbias_workspace_size(shape) bytes (Delta and per-key sums of dS).  The
  * sums run in a fixed order: the result is deterministic.
  */
@@ -233,16 +233,29 @@ int ra_attn_merge(void* out_a, float* lse_a, const void* out_b, const float* lse
  * With P = exp(scale * q k^T + bias - lse) on the visible pairs and dS = P * (dout v^T - delta),
  * the call adds, in float32 and without the scale factor of dq and dk:
  *   dq_acc [B,Lq,H,D] += dS k,   dk_acc [B,Lk,H,D] += dS^T q,   dv_acc [B,Lk,H,D] += P^T dout.
- * init_dq = 1 (init_dkv = 1) starts dq_acc (dk_acc, dv_acc) at zero without reading it.  In a
- * ring, dq_acc stays with the queries while dk_acc and dv_acc travel with their K/V block and
- * return to its owner after the last step ("手把手拆解RingAttention", section 2).  The two
- * kernels run in order on the stream; RA_BF16 only.
+ * With a bias and dbias_acc != NULL (float32 [B,H,Lk], 4-byte aligned) the call also adds the
+ * block's per-key sums of dS (no scale factor), the bias gradient's share of each key:
+ *   dbias_acc[b,h,j] += sum_i dS_ij.
+ * init_dq = 1 (init_dkv = 1) starts dq_acc (dk_acc, dv_acc, dbias_acc) at zero without reading it.
+ * In a ring, dq_acc stays with the queries while dk_acc, dv_acc and dbias_acc travel with their K/V
+ * block and return to its owner after the last step ("手把手拆解RingAttention", section 2).  The
+ * two kernels run in order on the stream; RA_BF16 only.  dbias_acc without a bias: RA_ERR_ARG.
  */
 int ra_blockwise_attn_bwd_step(const void* q, const void* k, const void* v, const float* bias,
                                const int32_t* segment_ids, int64_t seg_len, int64_t q_pos0, int64_t kv_pos0,
                                int32_t causal, const float* lse, const float* delta, const void* dout, float* dq_acc,
-                               float* dk_acc, float* dv_acc, int32_t init_dq, int32_t init_dkv, const ra_shape* shape,
-                               void* stream);
+                               float* dk_acc, float* dv_acc, float* dbias_acc, int32_t init_dq, int32_t init_dkv,
+                               const ra_shape* shape, void* stream);
+
+/* A K/V block's share of the bias gradient from the per-key sums it carried round the ring
+ * (dbias_acc of ra_blockwise_attn_bwd_step): its keys sit at global positions kv_pos0 + j, so
+ *   dbias[h, t] (+)= sum over b and j with (kv_pos0 + j) mod bias_len = t of key_sums[b,h,j]
+ * key_sums [B,H,Lk] float32 with Lk = shape.kv_len, dbias [H, bias_len] float32 (shape.bias_len >= 1);
+ * accumulate = 1 adds to dbias (one call per block: the blocks' shares sum to the whole gradient; on
+ * several devices the per-device results are summed), 0 overwrites it.  A fixed summation order:
+ * deterministic.  Any dtype; kv_pos0 >= 0. */
+int ra_blockwise_attn_bwd_dbias_reduce(const float* key_sums, int64_t kv_pos0, float* dbias, int32_t accumulate,
+                                       const ra_shape* shape, void* stream);
 
 /* Gradients from the ring-step sums: dq = scale * dq_acc [B,Lq,H,D], dk = scale * dk_acc and
  * dv = dv_acc [B,Lk,H,D], converted to shape.dtype (scale: shape.scale, or 1/sqrt(head_dim)). */

@@ -17,6 +17,7 @@ from .api import (  # noqa: F401
     blockwise_attn_fwd_finalize,
     attn_merge,
     blockwise_attn_bwd_step,
+    blockwise_attn_bwd_dbias_reduce,
     blockwise_attn_bwd_dbias,
     blockwise_attn_bwd_noalloc,
     blockwise_ffn_fwd,

@@ -56,7 +56,8 @@ def load_library():
         "ra_blockwise_attn_fwd_step": [P, P, P, P, P, I64, I64, I64, I32, P, P, P, I32, SH, P],
         "ra_blockwise_attn_fwd_finalize": [P, P, P, P, P, SH, P],
         "ra_attn_merge": [P, P, P, P, SH, P],
-        "ra_blockwise_attn_bwd_step": [P, P, P, P, P, I64, I64, I64, I32, P, P, P, P, P, P, I32, I32, SH, P],
+        "ra_blockwise_attn_bwd_step": [P, P, P, P, P, I64, I64, I64, I32, P, P, P, P, P, P, P, I32, I32, SH, P],
+        "ra_blockwise_attn_bwd_dbias_reduce": [P, I64, P, I32, SH, P],
         "ra_blockwise_attn_bwd_finalize": [P, P, P, P, P, P, SH, P],
         "ra_blockwise_attn_bwd_dbias": [P, P, P, P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, P, SZ, SH, P],
         "ra_blockwise_ffn_fwd": [P, P, P, P, P, I64, I32, I32, I64, P, SZ, P],
@@ -411,9 +412,11 @@ def attn_merge(out_a, lse_a, out_b, lse_b):
 
 
 def blockwise_attn_bwd_step(q, k, v, lse, delta, dout, bias=None, segment_ids=None, *, q_pos0, kv_pos0, causal,
-                            dq_acc=None, dk_acc=None, dv_acc=None, init_dq=None, init_dkv=None, scale=None):
+                            dq_acc=None, dk_acc=None, dv_acc=None, dbias_acc=None, init_dq=None, init_dkv=None,
+                            scale=None):
     """One backward ring step (ra_blockwise_attn_bwd_step): add this K/V block's contributions to
-    the float32 sums dq_acc (of the queries q) and dk_acc, dv_acc (of the block).  A sum passed as
+    the float32 sums dq_acc (of the queries q) and dk_acc, dv_acc (of the block), and with a given
+    dbias_acc (float32 [batch, heads, block length]) the block's per-key sums of dS.  A sum passed as
     None is allocated and started at zero; init_dq / init_dkv (default: the sum was None) start a
     given one at zero.  Returns (dq_acc, dk_acc, dv_acc)."""
     lib = load_library()
@@ -429,15 +432,37 @@ def blockwise_attn_bwd_step(q, k, v, lse, delta, dout, bias=None, segment_ids=No
     _expect("dq_acc", dq_acc, q.shape, torch.float32)
     _expect("dk_acc", dk_acc, k.shape, torch.float32)
     _expect("dv_acc", dv_acc, k.shape, torch.float32)
+    if dbias_acc is not None:
+        if bias is None:
+            raise ValueError("dbias_acc needs a bias")
+        _expect("dbias_acc", dbias_acc, (k.shape[0], k.shape[2], k.shape[1]), torch.float32)
     _tensors(q, k, v, bias, None, extra=(("lse", lse), ("delta", delta), ("dout", dout), ("segment_ids", segment_ids),
-                                         ("dq_acc", dq_acc), ("dk_acc", dk_acc), ("dv_acc", dv_acc)))
+                                         ("dq_acc", dq_acc), ("dk_acc", dk_acc), ("dv_acc", dv_acc),
+                                         ("dbias_acc", dbias_acc)))
     shape = make_shape(q, k, ring_rank=0, scale=scale, bias=bias)
     seg_len = 0 if segment_ids is None else segment_ids.shape[1]
     _check(lib.ra_blockwise_attn_bwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(segment_ids), int(seg_len),
                                           int(q_pos0), int(kv_pos0), _causal(causal), _ptr(lse), _ptr(delta),
-                                          _ptr(dout), _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc), int(i_dq),
-                                          int(i_dkv), ctypes.byref(shape), _stream(q.device)))
+                                          _ptr(dout), _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc), _ptr(dbias_acc),
+                                          int(i_dq), int(i_dkv), ctypes.byref(shape), _stream(q.device)))
     return dq_acc, dk_acc, dv_acc
+
+
+def blockwise_attn_bwd_dbias_reduce(key_sums, kv_pos0, dbias, *, accumulate=True):
+    """ra_blockwise_attn_bwd_dbias_reduce: add (or write) one K/V block's share of the bias gradient,
+    from the per-key sums key_sums [batch, heads, block length] it carried round the ring (keys at
+    global positions kv_pos0 + j), into dbias [heads, bias_len].  Returns dbias."""
+    lib = load_library()
+    if key_sums.dim() != 3 or dbias.dim() != 2 or dbias.shape[0] != key_sums.shape[1]:
+        raise ValueError("key_sums [batch, heads, block length] and dbias [heads, bias_len] expected")
+    _expect("key_sums", key_sums, key_sums.shape, torch.float32)
+    _expect("dbias", dbias, dbias.shape, torch.float32)
+    _devices(("key_sums", key_sums), ("dbias", dbias))
+    B, H, Lk = key_sums.shape
+    shape = Shape(B, H, 64, -1, Lk, Lk, dbias.shape[1], 0.0, RA_F32)
+    _check(lib.ra_blockwise_attn_bwd_dbias_reduce(_ptr(key_sums), int(kv_pos0), _ptr(dbias), int(bool(accumulate)),
+                                                  ctypes.byref(shape), _stream(dbias.device)))
+    return dbias
 
 
 def blockwise_attn_bwd_finalize(dq_acc, dk_acc, dv_acc, *, dtype=torch.bfloat16, scale=None, dq=None, dk=None,

@@ -551,8 +551,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     wg_id_range(kseg_lo, kseg_hi, sWaveSeg, wave, lane, gseg_lo, gseg_hi);
   }
 
-  // with a bias (outside ring steps): the lane's part of sum_i dS_ij for its key, the bias gradient
-  constexpr bool KEYSUM = HAS_BIAS && !STEP;
+  // with a bias: the lane's part of sum_i dS_ij for its key, from which the bias gradient is formed
+  // (in a ring step the sums are added to the ones the K/V block carries)
+  constexpr bool KEYSUM = HAS_BIAS;
   float dsum[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) dsum[kb] = 0.f;
@@ -871,6 +872,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     tpb[NS - 1] = walk.pos_base;
   }
 
+  // per-key sums of dS (lanes l and l + 32 hold the same key for different queries): written, or in a
+  // ring step added to the sums the block carries
+  if constexpr (KEYSUM) {
+    if (p.dbias_keys) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float t = pair_sum(dsum[kb]);
+        const int64_t krow = wk0 + kb * 32 + l32;
+        if (hh == 0 && krow < p.Lb) {
+          float* dst = p.dbias_keys + (static_cast<int64_t>(b) * p.H + h) * p.Lk + static_cast<int64_t>(j) * p.Lb + krow;
+          *dst = (STEP && !p.init_dkv) ? *dst + t : t;
+        }
+      }
+    }
+  }
   // dK^T / dV^T accumulators: lane holds d = db*32 + 8*(v/4) + 4*hh + v%4 of key column l32
   if constexpr (STEP) {
     // unscaled float32 sums back to caller memory
@@ -894,18 +910,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
         }
     }
     return;
-  }
-  if constexpr (KEYSUM) {
-    if (p.dbias_keys) {
-      // lanes l and l + 32 hold the same key for different queries
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const float t = pair_sum(dsum[kb]);
-        const int64_t krow = wk0 + kb * 32 + l32;
-        if (hh == 0 && krow < p.Lb)
-          p.dbias_keys[(static_cast<int64_t>(b) * p.H + h) * p.Lk + static_cast<int64_t>(j) * p.Lb + krow] = t;
-      }
-    }
   }
   __bf16* __restrict__ dkp = static_cast<__bf16*>(p.dk);
   __bf16* __restrict__ dvp = static_cast<__bf16*>(p.dv);

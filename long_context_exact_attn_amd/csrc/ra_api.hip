@@ -358,7 +358,6 @@ static int bwd_full(const void* q, const void* k, const void* v, const float* bi
   size_t need = delta_bytes;
   if (dbias) {
     if (!bias) return fail(RA_ERR_ARG, "dbias needs a bias");
-    if (shape->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "dbias is implemented for RA_BF16 only");
     RA_TRY(need_ptr(dbias, static_cast<int64_t>(shape->heads) * shape->bias_len, "dbias", 4));
     need += static_cast<size_t>(shape->batch) * shape->heads * shape->kv_len * sizeof(float);
   }
@@ -457,8 +456,8 @@ int ra_blockwise_attn_fwd_step(const void* q, const void* k, const void* v, cons
 int ra_blockwise_attn_bwd_step(const void* q, const void* k, const void* v, const float* bias,
                                const int32_t* segment_ids, int64_t seg_len, int64_t q_pos0, int64_t kv_pos0,
                                int32_t causal, const float* lse, const float* delta, const void* dout, float* dq_acc,
-                               float* dk_acc, float* dv_acc, int32_t init_dq, int32_t init_dkv, const ra_shape* shape,
-                               void* stream) {
+                               float* dk_acc, float* dv_acc, float* dbias_acc, int32_t init_dq, int32_t init_dkv,
+                               const ra_shape* shape, void* stream) {
   RA_TRY(check_dims(shape));
   if (shape->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "ring steps are implemented for RA_BF16 only");
   if (shape->q_len != shape->kv_len)
@@ -487,6 +486,10 @@ int ra_blockwise_attn_bwd_step(const void* q, const void* k, const void* v, cons
   RA_TRY(need_ptr(dq_acc, c.q_elems, "dq_acc", 16));
   RA_TRY(need_ptr(dk_acc, c.kv_elems, "dk_acc", 16));
   RA_TRY(need_ptr(dv_acc, c.kv_elems, "dv_acc", 16));
+  if (dbias_acc) {
+    if (!bias) return fail(RA_ERR_ARG, "dbias_acc needs a bias");
+    RA_TRY(need_ptr(dbias_acc, static_cast<int64_t>(shape->batch) * shape->heads * shape->kv_len, "dbias_acc", 4));
+  }
   if (c.rows == 0) return ok();
   c.p.q = q;
   c.p.k = k;
@@ -504,9 +507,29 @@ int ra_blockwise_attn_bwd_step(const void* q, const void* k, const void* v, cons
   c.p.dv_acc = dv_acc;
   c.p.init_dq = init_dq;
   c.p.init_dkv = init_dkv;
+  c.p.dbias_keys = dbias_acc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   RA_TRY(hip_status(ra::launch_bwd_dkdv_step_mfma(c.p, st), "dK/dV ring step launch"));
   return hip_status(ra::launch_bwd_dq_step_mfma(c.p, st), "dQ ring step launch");
+}
+
+int ra_blockwise_attn_bwd_dbias_reduce(const float* key_sums, int64_t kv_pos0, float* dbias, int32_t accumulate,
+                                       const ra_shape* shape, void* stream) {
+  RA_TRY(check_dims(shape));
+  if (shape->bias_len < 1 || shape->bias_len >= kMaxPos)
+    return fail(RA_ERR_ARG, "bias_len %lld must be in [1, 2^30)", (long long)shape->bias_len);
+  if (kv_pos0 < 0 || kv_pos0 + shape->kv_len >= kMaxPos)
+    return fail(RA_ERR_ARG, "kv_pos0 must be >= 0 and kv_pos0 + kv_len below 2^30");
+  if (accumulate != 0 && accumulate != 1) return fail(RA_ERR_ARG, "accumulate must be 0 or 1 (got %d)", accumulate);
+  const int64_t nk = static_cast<int64_t>(shape->batch) * shape->heads * shape->kv_len;
+  const int64_t nb = static_cast<int64_t>(shape->heads) * shape->bias_len;
+  if ((nb + 255) / 256 > 0x7fffffffLL) return fail(RA_ERR_SHAPE, "problem too large for one launch");
+  RA_TRY(need_ptr(key_sums, nk, "key_sums", 4));
+  RA_TRY(need_ptr(dbias, nb, "dbias", 4));
+  if (nb == 0) return ok();
+  return hip_status(ra::launch_bias_grad_block(key_sums, dbias, shape->batch, shape->heads, shape->kv_len, kv_pos0,
+                                               shape->bias_len, accumulate, static_cast<hipStream_t>(stream)),
+                    "dbias reduce launch");
 }
 
 int ra_blockwise_attn_bwd_finalize(const float* dq_acc, const float* dk_acc, const float* dv_acc, void* dq, void* dk,

@@ -59,7 +59,8 @@ struct Params {
   float* dk_acc;            // [B, Lk, H, D]
   float* dv_acc;            // [B, Lk, H, D]
   int32_t init_dq, init_dkv;   // 1: the sums start at zero (the incoming ones are not read)
-  // bias gradient (ra_blockwise_attn_bwd_dbias): per-key sums of dS over the queries, [B, H, Lk]
+  // bias gradient: per-key sums of dS over the queries, [B, H, Lk] (ra_blockwise_attn_bwd_dbias), or the
+  // sums one K/V block carries round a ring, [B, H, block length] (ra_blockwise_attn_bwd_step)
   float* dbias_keys;
 };
 
@@ -205,5 +206,7 @@ hipError_t ffn_backward(const __bf16* x, const __bf16* w1, const __bf16* w3, con
                         char* ws, hipStream_t st);
 hipError_t launch_bias_grad(const float* key_sums, float* dbias, int B, int H, int64_t Lk, int64_t bias_len,
                             hipStream_t st);
+hipError_t launch_bias_grad_block(const float* key_sums, float* dbias, int B, int H, int64_t Lb, int64_t kv_pos0,
+                                  int64_t bias_len, int accumulate, hipStream_t st);
 
 }  // namespace ra

@@ -231,6 +231,7 @@ __global__ __launch_bounds__(kLanes) void dkdv_simt_kernel(Params p) {
   const int kseg = (HAS_SEG && valid) ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
   const float bias_l2 = (HAS_BIAS && valid) ? p.bias[h * p.bias_len + key % p.bias_len] * kLog2e : 0.f;
   const float c = p.scale * kLog2e;
+  float dsum = 0.f;   // with a bias: sum_i dS_ij of this key, from which the bias gradient is formed
 
   QueryWalk walk;
   // the first query able to see this thread's key, and the first able to see the tile's first key
@@ -271,7 +272,9 @@ __global__ __launch_bounds__(kLanes) void dkdv_simt_kernel(Params p) {
         dp = __builtin_fmaf(sG[i][d], vr[d], dp);
       }
       const float pr = __builtin_amdgcn_exp2f(s * c + bias_l2 - sL[i]);
-      const float ds = pr * (dp - sD[i]) * p.scale;
+      const float ds0 = pr * (dp - sD[i]);
+      if (HAS_BIAS) dsum += ds0;
+      const float ds = ds0 * p.scale;
       for (int d = 0; d < D; ++d) {
         dv[d] = __builtin_fmaf(pr, sG[i][d], dv[d]);
         dk[d] = __builtin_fmaf(ds, sQ[i][d], dk[d]);
@@ -279,6 +282,7 @@ __global__ __launch_bounds__(kLanes) void dkdv_simt_kernel(Params p) {
     }
   }
   if (!valid) return;
+  if (HAS_BIAS && p.dbias_keys) p.dbias_keys[(static_cast<int64_t>(b) * p.H + h) * p.Lk + key] = dsum;
   T* dkp = static_cast<T*>(p.dk) + koff;
   T* dvp = static_cast<T*>(p.dv) + koff;
   for (int d = 0; d < D; ++d) {
@@ -506,6 +510,34 @@ __global__ __launch_bounds__(256) void bias_grad_kernel(const float* __restrict_
     for (int64_t j = t; j < Lk; j += nb) acc += row[j];
   }
   dbias[i] = acc;
+}
+
+// One K/V block's share of dbias: the block's keys sit at global positions kv_pos0 + j, so key j feeds
+// bias entry t = (kv_pos0 + j) mod bias_len; one lane per (h, t), a fixed summation order.  accumulate:
+// add to dbias (the blocks of a ring, one call each), else overwrite it.
+__global__ __launch_bounds__(256) void bias_grad_block_kernel(const float* __restrict__ key_sums,
+                                                              float* __restrict__ dbias, int B, int H, int64_t Lb,
+                                                              int64_t kv_pos0, int64_t nb, int accumulate) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(H) * nb) return;
+  const int h = static_cast<int>(i / nb);
+  const int64_t t = i % nb;
+  const int64_t j0 = ((t - kv_pos0 % nb) % nb + nb) % nb;   // first j of the block with (kv_pos0 + j) % nb == t
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const float* row = key_sums + (static_cast<int64_t>(b) * H + h) * Lb;
+    for (int64_t j = j0; j < Lb; j += nb) acc += row[j];
+  }
+  dbias[i] = accumulate ? dbias[i] + acc : acc;
+}
+
+hipError_t launch_bias_grad_block(const float* key_sums, float* dbias, int B, int H, int64_t Lb, int64_t kv_pos0,
+                                  int64_t bias_len, int accumulate, hipStream_t st) {
+  const int64_t n = static_cast<int64_t>(H) * bias_len;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(bias_grad_block_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, key_sums,
+                     dbias, B, H, Lb, kv_pos0, bias_len, accumulate);
+  return hipGetLastError();
 }
 
 hipError_t launch_bias_grad(const float* key_sums, float* dbias, int B, int H, int64_t Lk, int64_t bias_len,

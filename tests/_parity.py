@@ -88,6 +88,22 @@ def assert_close(name, got, ref, dtype, strict=True):
         assert rel <= tol["rel_rms"], msg
 
 
+def assert_close_sums(name, got, ref):
+    """Gradients that are sums over many products (the bias gradient, the feed-forward's weight
+    gradients): the benchmark spec bounds applied to the gradient normalised by its own scale, i.e.
+    max |got - ref| <= 2e-2 max|ref| + 1e-3 and relative RMS <= 1e-2.  (Their size grows with the
+    number of summed terms, so a fixed absolute bound would say nothing at large sizes.)"""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    max_abs, rel = errors(got, ref)
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    msg = f"{name}: max_abs={max_abs:.3e} rel_rms={rel:.3e} max|ref|={scale:.3g}"
+    print(msg, flush=True)
+    assert np.all(np.isfinite(got)), name + ": non-finite values"
+    assert max_abs <= 2e-2 * scale + 1e-3, msg
+    assert rel <= 1e-2, msg
+
+
 def assert_lse(got, ref, dtype):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

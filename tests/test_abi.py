@@ -202,9 +202,10 @@ def test_bwd_step_validation():
     S = lambda **kw: api.Shape(**{**dict(batch=1, heads=2, head_dim=64, ring_rank=-1, q_len=512, kv_len=512,  # noqa
                                          bias_len=0, scale=0.0, dtype=api.RA_BF16), **kw})
 
-    def step(shape, seg=None, seg_len=0, q_pos0=512, kv_pos0=0, i_dq=1, i_dkv=1, dv=None, delta=FAKE):
-        return lib.ra_blockwise_attn_bwd_step(FAKE, FAKE, FAKE, None, seg, seg_len, q_pos0, kv_pos0, 1, FAKE, delta,
-                                              FAKE, FAKE, FAKE, dv, i_dq, i_dkv, ctypes.byref(shape), None)
+    def step(shape, seg=None, seg_len=0, q_pos0=512, kv_pos0=0, i_dq=1, i_dkv=1, dv=None, delta=FAKE, dbias=None,
+             bias=None):
+        return lib.ra_blockwise_attn_bwd_step(FAKE, FAKE, FAKE, bias, seg, seg_len, q_pos0, kv_pos0, 1, FAKE, delta,
+                                              FAKE, FAKE, FAKE, dv, dbias, i_dq, i_dkv, ctypes.byref(shape), None)
 
     # dv_acc stays NULL in every call: none can reach a launch
     assert step(S(kv_len=256)) == -2 and b"equal query and key" in lib.ra_last_error()
@@ -216,6 +217,16 @@ def test_bwd_step_validation():
     assert step(S(), delta=None) == -1 and b"delta" in lib.ra_last_error()
     assert step(S()) == -1 and b"dv_acc" in lib.ra_last_error()
     assert step(S(batch=0)) == 0
+    # per-key dS sums for the bias gradient need a bias
+    assert step(S(), dv=FAKE, dbias=FAKE) == -1 and b"dbias_acc needs a bias" in lib.ra_last_error()
+
+    # the block's share of dbias: argument checks (dbias stays NULL: nothing is launched)
+    def red(shape, kv_pos0=0, acc=1, dbias=None):
+        return lib.ra_blockwise_attn_bwd_dbias_reduce(FAKE, kv_pos0, dbias, acc, ctypes.byref(shape), None)
+    assert red(S(bias_len=0)) == -1 and b"bias_len" in lib.ra_last_error()
+    assert red(S(bias_len=7), kv_pos0=-1) == -1
+    assert red(S(bias_len=7), acc=2) == -1
+    assert red(S(bias_len=7)) == -1 and b"dbias" in lib.ra_last_error()
 
     s = S()
     rc = lib.ra_blockwise_attn_bwd_finalize(FAKE, FAKE, FAKE, FAKE, FAKE, None, ctypes.byref(s), None)
@@ -241,8 +252,9 @@ def test_dbias_validation():
     assert call(api.Shape(1, 2, 64, -1, 1024, 1024, 100, 0.0, api.RA_F32), dv=None) == -1   # dv checked first
     assert call(s, dv=FAKE) == -4 and b"workspace" in lib.ra_last_error()
     assert call(s, dv=FAKE, ws=FAKE, ws_bytes=need - 4) == -4
+    # float32 is supported: with dv NULL the float32 call is refused for dv, not for its dtype
     f32 = api.Shape(1, 2, 64, -1, 1024, 1024, 100, 0.0, api.RA_F32)
-    assert call(f32, dv=FAKE, ws=FAKE, ws_bytes=need) == -3
+    assert call(f32, ws=FAKE, ws_bytes=need) == -1 and b"dv" in lib.ra_last_error()
 
 
 @needs_cpu

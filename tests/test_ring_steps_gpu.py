@@ -154,13 +154,18 @@ def test_step_errors(gpu):
 
 
 # ------------------------------------------------------------------ backward ring steps
-def _ring_backward(w, t, out, lse, skip_future=True):
+def _ring_backward(w, t, out, lse, skip_future=True, with_dbias=False):
     """All ranks of a ring on one GPU, one ra_blockwise_attn_bwd_step per (rank, step): dQ sums
-    stay with each rank's queries, dK / dV sums travel with their block."""
+    stay with each rank's queries, dK / dV sums (and, with_dbias, the per-key sums of dS) travel with
+    their block.  with_dbias also returns dbias, the blocks' shares added in block order."""
     n, lb = w.n_ring, w.block_len
     delta = ra.blockwise_attn_bwd_preprocess(out, t["dout"])
     dq_acc = [None] * n
     dkv_acc = [None] * n
+    kb_sums = [None] * n
+    if with_dbias:
+        for j in range(n):
+            kb_sums[j] = torch.full((w.batch, w.heads, lb), float("nan"), device=t["q"].device)
     for r in range(n):
         rows = slice(r * lb, (r + 1) * lb)
         q_r, g_r = t["q"][:, rows].contiguous(), t["dout"][:, rows].contiguous()
@@ -171,15 +176,22 @@ def _ring_backward(w, t, out, lse, skip_future=True):
                 continue
             kb, vb = _block(t["k"], j, lb), _block(t["v"], j, lb)
             dk_a, dv_a = dkv_acc[j] if dkv_acc[j] is not None else (None, None)
+            first_visit = dkv_acc[j] is None
             dq_acc[r], dk_a, dv_a = ra.blockwise_attn_bwd_step(
                 q_r, kb, vb, lse_r, dl_r, g_r, t["bias"], t["segment_ids"], q_pos0=r * lb, kv_pos0=j * lb,
-                causal=w.causal, dq_acc=dq_acc[r], dk_acc=dk_a, dv_acc=dv_a)
+                causal=w.causal, dq_acc=dq_acc[r], dk_acc=dk_a, dv_acc=dv_a, dbias_acc=kb_sums[j],
+                init_dkv=first_visit)
             dkv_acc[j] = (dk_a, dv_a)
     grads = [ra.blockwise_attn_bwd_finalize(dq_acc[i], *dkv_acc[i]) for i in range(n)]
     dq = torch.cat([g[0] for g in grads], dim=1)
     dk = torch.cat([g[1] for g in grads], dim=1)
     dv = torch.cat([g[2] for g in grads], dim=1)
-    return dq, dk, dv
+    if not with_dbias:
+        return dq, dk, dv
+    dbias = torch.full_like(t["bias"], float("nan"))
+    for j in range(n):
+        ra.blockwise_attn_bwd_dbias_reduce(kb_sums[j], j * lb, dbias, accumulate=j > 0)
+    return dq, dk, dv, dbias
 
 
 BWD_CASES = [
@@ -207,6 +219,35 @@ def test_bwd_step_ring_matches_oracle_and_fused(gpu, name, kw):
     for gname, g, f, r in (("dq", dq, fq, rdq), ("dk", dk, fk, rdk), ("dv", dv, fv, rdv)):
         P.assert_close(f"{name} {gname} steps vs oracle", P.np64(g), r, "bf16", strict=False)
         P.assert_close(f"{name} {gname} steps vs fused", P.np64(g), P.np64(f), "bf16", strict=False)
+
+
+DBIAS_STEP_CASES = [
+    ("bias-causal", dict(kv_len=2048, n_ring=4, bias_len=300)),
+    ("bias-seg-noncausal", dict(kv_len=1536, n_ring=3, causal=False, bias_len=64, segments="docs", doc_len=(20, 400))),
+    ("bias-longer-than-block", dict(kv_len=1024, n_ring=4, bias_len=700, segments="scattered")),
+    ("bias-d128-batch2-blocks", dict(head_dim=128, batch=2, heads=3, kv_len=1200, n_ring=3, bias_len=100, causal=40)),
+]
+
+
+@pytest.mark.parametrize("name,kw", DBIAS_STEP_CASES, ids=[c[0] for c in DBIAS_STEP_CASES])
+def test_bwd_step_ring_bias_gradient(gpu, name, kw):
+    # the per-key sums of dS travel with their K/V block; each block's share is reduced into dbias with the
+    # block's global key positions (bias entry (kv_pos0 + j) mod bias_len)
+    w = W.small(name, backward=True, **kw)
+    t = P.make(w, gpu)
+    out, lse = P.gpu_forward(w, t)
+    dq, dk, dv, db = _ring_backward(w, t, out, lse, with_dbias=True)
+    kwr = dict(n_ring=w.n_ring, q_chunk=w.q_chunk, k_chunk=w.k_chunk, causal=w.causal, ring_rank=w.ring_rank)
+    fdb = ra.blockwise_attn_bwd_dbias(t["q"], t["k"], t["v"], out, lse, t["dout"], t["bias"], t["segment_ids"],
+                                      **kwr)[3]
+    torch.cuda.synchronize()
+    d = P.oracle_inputs(t)
+    import oracle
+    ref = oracle.bias_grad(d["q"], d["k"], d["v"], d["dout"], q_pos=w.q_positions(), causal=w.causal,
+                           bias=d["bias"], segment_ids=d["segment_ids"])
+    got = db.double().cpu().numpy()
+    P.assert_close_sums(f"{name} dbias steps vs oracle", got, ref)
+    P.assert_close_sums(f"{name} dbias steps vs fused", got, fdb.double().cpu().numpy())
 
 
 def test_bwd_step_future_block_is_a_no_op(gpu):
