@@ -61,7 +61,7 @@
  *    execution surface at the caller's next synchronisation.
  *  - Thread safety.  The attention entry points keep no state apart from the
  *    per-thread error string; concurrent calls on different streams are safe.
- *    The feed-forward entry points keep one rocBLAS handle per device.
+ *    The feed-forward entry points are stateless too.
  */
 #ifndef RA_ATTN_H
 #define RA_ATTN_H
@@ -269,16 +269,17 @@ int ra_blockwise_attn_bwd_finalize(const float* dq_acc, const float* dk_acc, con
  *   out = W2 (silu(W1 x) * (W3 x)),   silu(a) = a / (1 + exp(-a)),
  * computed over chunks of `chunk` tokens so that the [tokens, d_ff] intermediate only ever
  * exists for one chunk (the result does not depend on the chunk).  bfloat16 tensors, float32
- * accumulation; the projections W1 x and W3 x, the gated activation h and the gradients of the
+ * accumulation on the library's own MFMA products; the gate silu(g) * u is formed in the epilogue
+ * of the product that makes g and u (in float32), and its derivative in the epilogue of the product
+ * that makes dh.  The gated activation h, the backward's g and u and the gradients of the
  * intermediate are rounded to bfloat16 between the products.
  *   x, out, dout, dx: [tokens, d_model];  w1, w3: [d_ff, d_model];  w2: [d_model, d_ff]
  *   (row-major, a linear layer's [out, in]);  dw1, dw3, dw2: float32, same shapes as the weights.
- * d_model and d_ff are multiples of 4; chunk * d_ff < 2^31.  The workspace (device, 256-byte
+ * d_model and d_ff are multiples of 8; chunk * d_ff < 2^31.  The workspace (device, 256-byte
  * aligned) holds ra_blockwise_ffn_workspace_size(...) bytes (backward = 1 for the backward).
  * The backward recomputes each chunk's intermediate, writes dx and overwrites dw1, dw3, dw2
- * with the sums over all tokens.  The GEMMs run on rocBLAS: the library keeps one rocBLAS
- * handle per device for the life of the process, and calls of these two entry points are
- * serialised by a lock.
+ * with the sums over all tokens; the weight gradients' products are split over the chunk's
+ * tokens into partial sums in the workspace, added in a fixed order (deterministic).
  */
 size_t ra_blockwise_ffn_workspace_size(int64_t tokens, int32_t d_model, int32_t d_ff, int64_t chunk,
                                        int32_t backward);
@@ -292,7 +293,7 @@ int ra_blockwise_ffn_bwd(const void* x, const void* w1, const void* w3, const vo
 /* Description of the last error on the calling thread ("" after a success). */
 const char* ra_last_error(void);
 
-/* Library ABI version: 1. */
+/* Library ABI version: 2. */
 int32_t ra_abi_version(void);
 
 #ifdef __cplusplus

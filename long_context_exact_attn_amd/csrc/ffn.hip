@@ -1,94 +1,167 @@
-// Blockwise feed-forward (SwiGLU), bfloat16 in / float32 accumulate.
+// Blockwise feed-forward (SwiGLU), bfloat16 in / float32 accumulate, on this library's own MFMA
+// GEMM (gemm.cuh).
 //
 // The feed-forward is applied chunk by chunk over the tokens ("RingAttention核心功能全解析",
 // 快速上手, blockwise_feedforward), so the [tokens, d_ff] intermediate exists for one chunk at a
-// time.  The three products per chunk are plain GEMMs and run on rocBLAS (bf16 inputs, float32
-// accumulation); the SwiGLU gate and its derivative are hand-written elementwise kernels between
-// them.  Matrices are row-major; a row-major [r, c] matrix is handed to the column-major GEMM as
-// its [c, r] transpose, so y = x W^T for a row-major weight W [out, in] becomes the column-major
-// product Y^T = W_cm^T X^T with W_cm = W^T.
-#include <rocblas/rocblas.h>
-
-#include <mutex>
-
-#include "ra_common.cuh"
+// time.  Matrices are row-major: x, out, dout, dx [tokens, d]; W1, W3 [f, d]; W2 [d, f].
+//
+// Forward, per chunk:
+//   h = silu(x W1^T) * (x W3^T)   one GEMM against W1 and W3 together: each workgroup's B tile
+//                                 holds 64 rows of W1 and the same 64 rows of W3, so a lane owns g
+//                                 and u of the same (token, j) and the gate runs in the epilogue
+//   out = h W2^T
+// Backward, per chunk (the intermediate is recomputed):
+//   dh = dout W2                  stored, bfloat16
+//   [g u] = x [W1; W3]^T          epilogue: dg = dh u silu'(g), du = dh silu(g), h = silu(g) u
+//   dx = [dg du] [W1; W3]
+//   [dW1; dW3] (+)= [dg du]^T x,  dW2 (+)= dout^T h     float32, split over K (tokens) into partial
+//                                 sums that a small kernel adds in a fixed order (deterministic)
+#include "gemm.cuh"
 
 namespace ra {
 namespace {
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+using gemm::Operand;
 
-__device__ __forceinline__ float sigmoid(float a) { return 1.f / (1.f + __expf(-a)); }
+constexpr int64_t kNone = INT64_MAX;
 
-// The gate and up projections of a chunk come out of one GEMM against the stacked weight
-// [W1; W3]: column j of gu (column-major [2 d_ff, chunk]) holds g = W1 x_j in rows [0, d_ff) and
-// u = W3 x_j in rows [d_ff, 2 d_ff).  Four elements of a column per lane (d_ff % 4 == 0).
+__device__ __forceinline__ float sigmoidf_(float a) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-a * kLog2e));
+}
 
-// h[:, j] = silu(g) * u
-__global__ __launch_bounds__(256) void swiglu_fwd_kernel(const __bf16* __restrict__ gu, __bf16* __restrict__ h, int f,
-                                                         int64_t n4) {
-  const int64_t i4 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i4 >= n4) return;
-  const int64_t e = 4 * i4, j = e / f, r = e % f;
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(gu + j * 2 * f + r);
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(gu + j * 2 * f + f + r);
-  bf16x4 o;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float g = (float)a[k];
-    o[k] = (__bf16)(g * sigmoid(g) * (float)b[k]);
+// B rows of the gate GEMM: tile rows 32 b + r (b = 0..7) hold W1 (b even) or W3 (b odd) row
+// j = n0 / 2 + 32 (b / 2) + r, as rows j and f + j of the virtual stacked [W1; W3]
+struct GateRows {
+  int64_t f;
+  __device__ int64_t operator()(int64_t n0, int r) const {
+    const int b = r >> 5;
+    const int64_t j = n0 / 2 + 32 * (b >> 1) + (r & 31);
+    if (j >= f) return 2 * f;   // past the last row: the zero chunk
+    return (b & 1) ? f + j : j;
   }
-  *reinterpret_cast<bf16x4*>(h + e) = o;
-}
+};
 
-// dg = dh * u * silu'(g), du = dh * silu(g), with silu'(g) = s (1 + g (1 - s)), s = sigmoid(g);
-// written in the stacked layout of gu, so that one GEMM against [W1; W3] gives dx
-__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const __bf16* __restrict__ dh, const __bf16* __restrict__ gu,
-                                                         __bf16* __restrict__ dgdu, int f, int64_t n4) {
-  const int64_t i4 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i4 >= n4) return;
-  const int64_t e = 4 * i4, j = e / f, r = e % f;
-  const bf16x4 d = *reinterpret_cast<const bf16x4*>(dh + e);
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(gu + j * 2 * f + r);
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(gu + j * 2 * f + f + r);
-  bf16x4 og, ou;
+struct StoreBf16 {
+  __bf16* C;
+  int64_t ldc;
+  __device__ void operator()(const f32x16 (&acc)[4][2], int64_t mb0, int64_t nb0, int, int l32, int hh, int64_t M,
+                             int64_t N) const {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float g = (float)a[k], u = (float)b[k], dd = (float)d[k];
-    const float s = sigmoid(g);
-    og[k] = (__bf16)(dd * u * s * (1.f + g * (1.f - s)));
-    ou[k] = (__bf16)(dd * g * s);
+    for (int b = 0; b < 2; ++b) {
+      const int64_t n = nb0 + 32 * b + l32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t m = mb0 + 32 * a + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (m < M) C[m * ldc + n] = (__bf16)acc[a][b][v];
+        }
+    }
   }
-  *reinterpret_cast<bf16x4*>(dgdu + j * 2 * f + r) = og;
-  *reinterpret_cast<bf16x4*>(dgdu + j * 2 * f + f + r) = ou;
+};
+
+// h = silu(g) u into H [M, f]: block b = 0 of the wave holds g, b = 1 holds u, j = nb0 / 2 + l32
+struct GateFwd {
+  __bf16* H;
+  int64_t f;
+  __device__ void operator()(const f32x16 (&acc)[4][2], int64_t mb0, int64_t nb0, int, int l32, int hh, int64_t M,
+                             int64_t) const {
+    const int64_t j = nb0 / 2 + l32;
+    if (j >= f) return;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = mb0 + 32 * a + 8 * (v >> 2) + 4 * hh + (v & 3);
+        const float g = acc[a][0][v], u = acc[a][1][v];
+        if (m < M) H[m * f + j] = (__bf16)(g * sigmoidf_(g) * u);
+      }
+  }
+};
+
+// The backward's gate product [g u] = x [W1; W3]^T with the gate's derivative in its epilogue:
+// with dh = dout W2 already in DH [M, f] and s = sigmoid(g),
+//   dg = dh u s (1 + g (1 - s)),  du = dh g s   into DGDU [M, 2 f] (g's columns, then u's)
+//   h = g s u                                   into H [M, f]
+// so g and u never leave the registers.  One 32-row block at a time; its dh values are all loaded
+// before any result is stored (the pointers are declared not to alias, so the loads overlap).
+__device__ __forceinline__ void gate_bwd_block(const __bf16* __restrict__ DH, __bf16* __restrict__ DGDU,
+                                               __bf16* __restrict__ H, const f32x16 (&acc)[2], int64_t mrow0,
+                                               int64_t j, int hh, int64_t M, int64_t f) {
+  if (j >= f) return;
+  float dh[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t m = mrow0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+    dh[v] = m < M ? (float)DH[m * f + j] : 0.f;
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t m = mrow0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+    if (m >= M) continue;
+    const float g = acc[0][v], u = acc[1][v], s = sigmoidf_(g);
+    DGDU[m * 2 * f + j] = (__bf16)(dh[v] * u * s * (1.f + g * (1.f - s)));
+    DGDU[m * 2 * f + f + j] = (__bf16)(dh[v] * g * s);
+    H[m * f + j] = (__bf16)(g * s * u);
+  }
 }
 
-// One rocBLAS handle per device, created on first use and kept for the process.
-std::mutex g_blas_mutex;
-rocblas_handle g_blas[64] = {};
+struct GateBwd {
+  const __bf16* DH;
+  __bf16* DGDU;
+  __bf16* H;
+  int64_t f;
+  __device__ void operator()(const f32x16 (&acc)[4][2], int64_t mb0, int64_t nb0, int, int l32, int hh, int64_t M,
+                             int64_t) const {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) gate_bwd_block(DH, DGDU, H, acc[a], mb0 + 32 * a, nb0 / 2 + l32, hh, M, f);
+  }
+};
 
-hipError_t blas_handle(rocblas_handle* out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) return hipErrorNotInitialized;
-  *out = g_blas[dev];
-  return hipSuccess;
-}
+// float32 result rows [0, rsplit) into out1 and the rest into out2 (row length ldo): written
+// (splits == 1) or as split `split`'s partial sum into part [splits][M][N]
+struct F32Out {
+  float* out1;
+  float* out2;
+  int64_t rsplit, ldo;
+  float* part;
+  int splits;
+  int accumulate;
+  __device__ void operator()(const f32x16 (&acc)[4][2], int64_t mb0, int64_t nb0, int split, int l32, int hh,
+                             int64_t M, int64_t N) const {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t n = nb0 + 32 * b + l32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t m = mb0 + 32 * a + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (m >= M) continue;
+          if (splits > 1) {
+            part[(static_cast<int64_t>(split) * M + m) * N + n] = acc[a][b][v];
+          } else {
+            float* o = m < rsplit ? out1 + m * ldo + n : out2 + (m - rsplit) * ldo + n;
+            *o = accumulate ? *o + acc[a][b][v] : acc[a][b][v];
+          }
+        }
+    }
+  }
+};
 
-// column-major C[m, n] = alpha op(A) op(B) + beta C, bf16 A and B, float32 accumulation
-hipError_t gemm(rocblas_handle hd, bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
-                const void* B, int64_t ldb, float beta, void* C, bool c_bf16, int64_t ldc) {
-  const float alpha = 1.f;
-  const rocblas_datatype ct = c_bf16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-  const rocblas_status s = rocblas_gemm_ex(
-      hd, ta ? rocblas_operation_transpose : rocblas_operation_none, tb ? rocblas_operation_transpose : rocblas_operation_none,
-      static_cast<rocblas_int>(m), static_cast<rocblas_int>(n), static_cast<rocblas_int>(k), &alpha, A,
-      rocblas_datatype_bf16_r, static_cast<rocblas_int>(lda), B, rocblas_datatype_bf16_r, static_cast<rocblas_int>(ldb),
-      &beta, C, ct, static_cast<rocblas_int>(ldc), C, ct, static_cast<rocblas_int>(ldc), rocblas_datatype_f32_r,
-      rocblas_gemm_algo_standard, 0, 0);
-  return s == rocblas_status_success ? hipSuccess : hipErrorLaunchFailure;
+// out (+)= sum over s = 0 .. splits - 1 of part[s] (in that order), rows split over out1 / out2
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, float* out1, float* out2,
+                                                            int64_t rsplit, int64_t ldo, int64_t M, int64_t N,
+                                                            int splits, int accumulate) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= M * N) return;
+  const int64_t m = i / N, n = i % N;
+  float* o = m < rsplit ? out1 + m * ldo + n : out2 + (m - rsplit) * ldo + n;
+  float s = accumulate ? *o : 0.f;
+  for (int k = 0; k < splits; ++k) s += part[static_cast<int64_t>(k) * M * N + i];
+  *o = s;
 }
 
 #define RA_HIP(x)                         \
@@ -97,7 +170,71 @@ hipError_t gemm(rocblas_handle hd, bool ta, bool tb, int64_t m, int64_t n, int64
     if (e_ != hipSuccess) return e_;      \
   } while (0)
 
-dim3 grid4(int64_t n4) { return dim3(static_cast<unsigned>((n4 + 255) / 256)); }
+int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+// C [M, N] of A [M, K] and B [K, N] on tiles_n column tiles (the gate GEMM's tiles hold 128 columns
+// of h); the B tile at column n0 lies inside B when n0 + BN <= N
+template <bool AK, bool BK_, typename Map, typename Epi>
+hipError_t run(const Operand& A, const Operand& B, int64_t M, int64_t N, int64_t K, int tiles_n, int splits, Map map,
+               Epi epi, hipStream_t st) {
+  const int tiles_m = cdiv(M, gemm::BM);
+  const int64_t kps = (cdiv(K, splits * gemm::BK)) * static_cast<int64_t>(gemm::BK);
+  const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n * splits;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((gemm::gemm_kernel<AK, BK_, Map, Epi>), dim3(static_cast<unsigned>(grid)), dim3(gemm::kThreadsG),
+                     0, st, A, B, M, N, K, tiles_m, tiles_n, splits, kps, N, map, epi);
+  return hipGetLastError();
+}
+
+constexpr int kMaxSplits = 4;   // the partial sums' extra traffic grows with the splits
+constexpr int kSlots = 256;   // workgroups resident at once: one 128 KiB-LDS workgroup per CU
+
+// K splits for the weight-gradient products: enough workgroups to fill the chip in whole rounds,
+// each split at least 512 deep
+int pick_splits(int64_t tiles, int64_t K) {
+  int best = 1;
+  double best_eff = 0.0;
+  for (int s = 1; s <= kMaxSplits; ++s) {
+    if (s > 1 && K / s < 512) break;
+    const int64_t wg = tiles * s;
+    const int64_t rounds = (wg + kSlots - 1) / kSlots;
+    const double eff = static_cast<double>(wg) / static_cast<double>(rounds * kSlots);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = s;
+    }
+  }
+  return best;
+}
+
+Operand op(const __bf16* base, int64_t ld, int64_t rows, int64_t kdim, const __bf16* base2 = nullptr,
+           int64_t split = kNone) {
+  Operand o;
+  o.base = base;
+  o.base2 = base2 ? base2 : base;
+  o.ld = ld;
+  o.split = split;
+  o.rows = rows;
+  o.kdim = kdim;
+  return o;
+}
+
+// the float32 weight-gradient product C [M, N] (+)= A B over the chunk's tokens, split over K
+template <typename Map>
+hipError_t weight_grad(const Operand& A, const Operand& B, int64_t M, int64_t N, int64_t K, float* out1, float* out2,
+                       int64_t rsplit, int accumulate, float* part, int splits, Map map, hipStream_t st) {
+  const int tiles_n = cdiv(N, gemm::BN);
+  F32Out epi{out1, out2, rsplit, N, part, splits, accumulate};
+  RA_HIP((run<false, false>(A, B, M, N, K, tiles_n, splits, map, epi, st)));
+  if (splits > 1) {
+    const int64_t n = M * N;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, part,
+                       out1, out2, rsplit, N, M, N, splits, accumulate);
+    RA_HIP(hipGetLastError());
+  }
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -107,46 +244,33 @@ FfnWorkspace ffn_workspace(int64_t tokens, int d_model, int d_ff, int64_t chunk,
   const size_t f = static_cast<size_t>(d_ff), d = static_cast<size_t>(d_model);
   FfnWorkspace w{};
   size_t off = 0;
-  w.w13 = off; off += up(2 * f * d * 2);       // [W1; W3], bf16
-  w.gu = off; off += up(2 * f * c * 2);        // gate and up projections of a chunk, bf16
-  w.h = off; off += up(f * c * 2);             // silu(g) * u, bf16
+  w.h = off; off += up(f * c * 2);             // silu(g) * u of a chunk, bf16
   if (backward) {
-    w.dh = off; off += up(f * c * 2);          // W2^T dout, bf16
+    w.gu = off; off += up(f * c * 2);          // dh = dout W2 of a chunk, bf16
     w.dgdu = off; off += up(2 * f * c * 2);    // gradients of g and u, stacked like gu, bf16
-    w.dw13 = off; off += up(2 * f * d * 4);    // [dW1; dW3] sums, float32
+    // partial sums of the split weight-gradient products
+    const int s13 = pick_splits(static_cast<int64_t>(cdiv(2 * f, gemm::BM)) * cdiv(d, gemm::BN), c);
+    const int s2 = pick_splits(static_cast<int64_t>(cdiv(d, gemm::BM)) * cdiv(f, gemm::BN), c);
+    const size_t p13 = s13 > 1 ? static_cast<size_t>(s13) * 2 * f * d : 0, p2 = s2 > 1 ? static_cast<size_t>(s2) * d * f : 0;
+    w.dw13 = off; off += up((p13 > p2 ? p13 : p2) * 4);
   }
   w.bytes = off;
   return w;
 }
 
-namespace {
-// [W1; W3] stacked (row-major [2 d_ff, d_model]) in the workspace
-hipError_t stack_weights(const __bf16* w1, const __bf16* w3, __bf16* w13, int d, int f, hipStream_t st) {
-  const size_t bytes = static_cast<size_t>(f) * d * sizeof(__bf16);
-  RA_HIP(hipMemcpyAsync(w13, w1, bytes, hipMemcpyDeviceToDevice, st));
-  return hipMemcpyAsync(w13 + static_cast<size_t>(f) * d, w3, bytes, hipMemcpyDeviceToDevice, st);
-}
-}  // namespace
-
 hipError_t ffn_forward(const __bf16* x, const __bf16* w1, const __bf16* w3, const __bf16* w2, __bf16* out,
                        int64_t tokens, int d, int f, int64_t chunk, char* ws, hipStream_t st) {
-  std::lock_guard<std::mutex> lock(g_blas_mutex);
-  rocblas_handle hd;
-  RA_HIP(blas_handle(&hd));
-  if (rocblas_set_stream(hd, st) != rocblas_status_success) return hipErrorInvalidValue;
   const FfnWorkspace w = ffn_workspace(tokens, d, f, chunk, false);
-  __bf16* w13 = reinterpret_cast<__bf16*>(ws + w.w13);
-  __bf16* gu = reinterpret_cast<__bf16*>(ws + w.gu);
   __bf16* h = reinterpret_cast<__bf16*>(ws + w.h);
-  RA_HIP(stack_weights(w1, w3, w13, d, f, st));
   for (int64_t t0 = 0; t0 < tokens; t0 += chunk) {
     const int64_t c = tokens - t0 < chunk ? tokens - t0 : chunk;
     const __bf16* xc = x + t0 * d;
-    RA_HIP(gemm(hd, true, false, 2 * f, c, d, w13, d, xc, d, 0.f, gu, true, 2 * f));   // [g; u]^T = [W1; W3] x^T
-    const int64_t n4 = static_cast<int64_t>(f) * c / 4;
-    hipLaunchKernelGGL(swiglu_fwd_kernel, grid4(n4), dim3(256), 0, st, gu, h, f, n4);
-    RA_HIP(hipGetLastError());
-    RA_HIP(gemm(hd, true, false, d, c, f, w2, f, h, f, 0.f, out + t0 * d, true, d));   // y^T = W2 h^T
+    // h = silu(x W1^T) * (x W3^T): B rows are those of the virtual [W1; W3] (split at f)
+    RA_HIP((run<true, true>(op(xc, d, c, d), op(w1, d, 2 * int64_t(f), d, w3, f), c, 2 * int64_t(f), d,
+                            cdiv(f, gemm::BN / 2), 1, GateRows{f}, GateFwd{h, f}, st)));
+    // out = h W2^T
+    RA_HIP((run<true, true>(op(h, f, c, f), op(w2, f, d, f), c, d, f, cdiv(d, gemm::BN), 1, gemm::LinearRows{},
+                            StoreBf16{out + t0 * d, d}, st)));
   }
   return hipSuccess;
 }
@@ -154,7 +278,6 @@ hipError_t ffn_forward(const __bf16* x, const __bf16* w1, const __bf16* w3, cons
 hipError_t ffn_backward(const __bf16* x, const __bf16* w1, const __bf16* w3, const __bf16* w2, const __bf16* dout,
                         __bf16* dx, float* dw1, float* dw3, float* dw2, int64_t tokens, int d, int f, int64_t chunk,
                         char* ws, hipStream_t st) {
-  std::lock_guard<std::mutex> lock(g_blas_mutex);
   if (tokens == 0) {
     // no token contributes: the weight gradients are zero
     RA_HIP(hipMemsetAsync(dw1, 0, sizeof(float) * f * d, st));
@@ -162,37 +285,36 @@ hipError_t ffn_backward(const __bf16* x, const __bf16* w1, const __bf16* w3, con
     RA_HIP(hipMemsetAsync(dw2, 0, sizeof(float) * d * f, st));
     return hipSuccess;
   }
-  rocblas_handle hd;
-  RA_HIP(blas_handle(&hd));
-  if (rocblas_set_stream(hd, st) != rocblas_status_success) return hipErrorInvalidValue;
   const FfnWorkspace w = ffn_workspace(tokens, d, f, chunk, true);
-  __bf16* w13 = reinterpret_cast<__bf16*>(ws + w.w13);
-  __bf16* gu = reinterpret_cast<__bf16*>(ws + w.gu);
   __bf16* h = reinterpret_cast<__bf16*>(ws + w.h);
-  __bf16* dh = reinterpret_cast<__bf16*>(ws + w.dh);
+  __bf16* dhb = reinterpret_cast<__bf16*>(ws + w.gu);
   __bf16* dgdu = reinterpret_cast<__bf16*>(ws + w.dgdu);
-  float* dw13 = reinterpret_cast<float*>(ws + w.dw13);
-  RA_HIP(stack_weights(w1, w3, w13, d, f, st));
+  float* part = reinterpret_cast<float*>(ws + w.dw13);
+  const int64_t F = f, F2 = 2 * int64_t(f), Dm = d;
   for (int64_t t0 = 0; t0 < tokens; t0 += chunk) {
     const int64_t c = tokens - t0 < chunk ? tokens - t0 : chunk;
-    const float acc = t0 == 0 ? 0.f : 1.f;   // weight gradients: the first chunk overwrites
+    const int acc = t0 == 0 ? 0 : 1;   // weight gradients: the first chunk writes, later ones add
     const __bf16* xc = x + t0 * d;
     const __bf16* dc = dout + t0 * d;
-    const int64_t n4 = static_cast<int64_t>(f) * c / 4;
-    // recompute the chunk's intermediate
-    RA_HIP(gemm(hd, true, false, 2 * f, c, d, w13, d, xc, d, 0.f, gu, true, 2 * f));
-    hipLaunchKernelGGL(swiglu_fwd_kernel, grid4(n4), dim3(256), 0, st, gu, h, f, n4);
-    RA_HIP(hipGetLastError());
-    RA_HIP(gemm(hd, false, false, f, c, d, w2, f, dc, d, 0.f, dh, true, f));               // dh^T = W2^T dout^T
-    hipLaunchKernelGGL(swiglu_bwd_kernel, grid4(n4), dim3(256), 0, st, dh, gu, dgdu, f, n4);
-    RA_HIP(hipGetLastError());
-    RA_HIP(gemm(hd, false, false, d, c, 2 * f, w13, d, dgdu, 2 * f, 0.f, dx + t0 * d, true, d));   // dx^T
-    RA_HIP(gemm(hd, false, true, d, 2 * f, c, xc, d, dgdu, 2 * f, acc, dw13, false, d));   // [dW1; dW3]^T += x^T [dg du]
-    RA_HIP(gemm(hd, false, true, f, d, c, h, f, dc, d, acc, dw2, false, f));               // dW2^T += h^T dout
+    // dh = dout W2 (W2 is [d, f] = [K, N])
+    RA_HIP((run<true, false>(op(dc, Dm, c, Dm), op(w2, F, F, Dm), c, F, Dm, cdiv(F, gemm::BN), 1, gemm::LinearRows{},
+                             StoreBf16{dhb, F}, st)));
+    // [g u] = x [W1; W3]^T, with the gate's derivative and h in the epilogue
+    RA_HIP((run<true, true>(op(xc, Dm, c, Dm), op(w1, Dm, F2, Dm, w3, F), c, F2, Dm, cdiv(F, gemm::BN / 2), 1,
+                            GateRows{F}, GateBwd{dhb, dgdu, h, F}, st)));
+    // dx = [dg du] [W1; W3] ([W1; W3] is [2 f, d] = [K, N], split at K = f)
+    RA_HIP((run<true, false>(op(dgdu, F2, c, F2), op(w1, Dm, Dm, F2, w3, F), c, Dm, F2, cdiv(Dm, gemm::BN), 1,
+                             gemm::LinearRows{}, StoreBf16{dx + t0 * d, Dm}, st)));
+    // [dW1; dW3] (+)= [dg du]^T x: A = [dg du] stored [c, 2 f] = [K, M]; B = x [c, d] = [K, N]
+    const int s13 = pick_splits(static_cast<int64_t>(cdiv(F2, gemm::BM)) * cdiv(Dm, gemm::BN), c);
+    RA_HIP(weight_grad(op(dgdu, F2, F2, c), op(xc, Dm, Dm, c), F2, Dm, c, dw1, dw3, F, acc, part, s13,
+                       gemm::LinearRows{}, st));
+    // dW2 (+)= dout^T h: A = dout stored [c, d] = [K, M]; B = h [c, f] = [K, N]
+    const int s2 = pick_splits(static_cast<int64_t>(cdiv(Dm, gemm::BM)) * cdiv(F, gemm::BN), c);
+    RA_HIP(weight_grad(op(dc, Dm, Dm, c), op(h, F, F, c), Dm, F, c, dw2, dw2, Dm, acc, part, s2, gemm::LinearRows{},
+                       st));
   }
-  const size_t bytes = sizeof(float) * f * d;
-  RA_HIP(hipMemcpyAsync(dw1, dw13, bytes, hipMemcpyDeviceToDevice, st));
-  return hipMemcpyAsync(dw3, dw13 + static_cast<size_t>(f) * d, bytes, hipMemcpyDeviceToDevice, st);
+  return hipSuccess;
 }
 
 }  // namespace ra

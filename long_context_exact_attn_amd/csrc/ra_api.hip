@@ -170,8 +170,8 @@ int32_t ra_abi_version(void) { return 2; }
 
 static int ffn_check(int64_t tokens, int32_t d_model, int32_t d_ff, int64_t chunk) {
   if (tokens < 0 || tokens >= kMaxPos) return fail(RA_ERR_SHAPE, "tokens must be in [0, 2^30) (got %lld)", (long long)tokens);
-  if (d_model < 4 || d_ff < 4 || d_model % 4 || d_ff % 4 || d_model > 65536 || d_ff > 262144)
-    return fail(RA_ERR_SHAPE, "d_model and d_ff must be multiples of 4 in [4, 65536] / [4, 262144] (got %d, %d)",
+  if (d_model < 8 || d_ff < 8 || d_model % 8 || d_ff % 8 || d_model > 65536 || d_ff > 262144)
+    return fail(RA_ERR_SHAPE, "d_model and d_ff must be multiples of 8 in [8, 65536] / [8, 262144] (got %d, %d)",
                 d_model, d_ff);
   if (chunk < 1) return fail(RA_ERR_ARG, "chunk must be >= 1 (got %lld)", (long long)chunk);
   const int64_t c = tokens < chunk ? tokens : chunk;

@@ -260,8 +260,9 @@ def test_dbias_validation():
 @needs_cpu
 def test_ffn_validation():
     lib = _lib()
-    # at least the chunk's gate/up projections and activation, bfloat16
-    assert lib.ra_blockwise_ffn_workspace_size(1000, 256, 704, 512, 0) >= 512 * 704 * (2 + 2 + 2)
+    # the forward holds the chunk's activation h (bfloat16); the backward also dh and the gradients of g, u
+    assert lib.ra_blockwise_ffn_workspace_size(1000, 256, 704, 512, 0) >= 512 * 704 * 2
+    assert lib.ra_blockwise_ffn_workspace_size(1000, 256, 704, 512, 1) >= 512 * 704 * (2 + 2 + 4)
     assert lib.ra_blockwise_ffn_workspace_size(1000, 256, 704, 512, 1) > lib.ra_blockwise_ffn_workspace_size(
         1000, 256, 704, 512, 0)
 
@@ -269,6 +270,7 @@ def test_ffn_validation():
         return lib.ra_blockwise_ffn_fwd(FAKE, FAKE, FAKE, FAKE, out, T, d, f, chunk, ws, ws_bytes, None)
 
     assert fwd(d=66) == -2
+    assert fwd(d=68) == -2 and b"multiples of 8" in lib.ra_last_error()
     assert fwd(f=0) == -2
     assert fwd(chunk=0) == -1
     assert fwd(T=-1) == -2
