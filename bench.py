@@ -401,22 +401,26 @@ def main():
     ex = {}
     if segn is None and not args.ring_steps:
         D_, HB_ = w.head_dim, w.heads * w.batch
-        nqb = 2 if w.head_dim == 64 else 1
-        e_fwd = M.executed_pairs_per_head(q_first, w.q_len, w.kv_len, w.causal, 32 * nqb, 64)
-        e_kv = M.executed_pairs_per_head(q_first, w.q_len, w.kv_len, w.causal,
-                                         128 if (w.head_dim == 64 and w.segments == "none") else 64, 32)
-        e_dq = M.executed_pairs_per_head(q_first, w.q_len, w.kv_len, w.causal, 32, 64)
+        if w.dtype == "bf16":
+            nqb = 2 if w.head_dim == 64 else 1
+            tiles = ((32 * nqb, 64), (128 if (w.head_dim == 64 and w.segments == "none") else 64, 32), (32, 64))
+        else:   # the float32 kernels: 16 x 16 tiles throughout
+            tiles = ((16, 16), (16, 16), (16, 16))
+        e_fwd, e_kv, e_dq = (M.executed_pairs_per_head(q_first, w.q_len, w.kv_len, w.causal, tq, tk)
+                             for tq, tk in tiles)
         if None not in (e_fwd, e_kv, e_dq):
             ex = {"fwd": 4 * D_ * e_fwd * HB_, "bwd_dkdv": 8 * D_ * e_kv * HB_, "bwd_dq": 6 * D_ * e_dq * HB_}
     kernel_flops = {"fwd": fl["fwd"], "bwd_dkdv": fl["dkdv"], "bwd_dq": fl["dq"], "bwd_steps": fl["dkdv"] + fl["dq"]}
     total_flops = fl["fwd"] if args.fwd_only else fl["fwd_bwd"]
     value = total_flops / (ms_step * 1e-3) / 1e12
+    # a contraction is priced against the matrix unit's peak for its own dtype
+    peak = M.PEAK_BF16_TFLOPS if w.dtype == "bf16" else M.PEAK_F32_TFLOPS
     kernels = {}
     for n in names:
         entry = {"ms": round(per[n], 4)}
         if n in kernel_flops:
             entry["tflops"] = round(kernel_flops[n] / (per[n] * 1e-3) / 1e12, 2)
-            entry["frac_peak"] = round(entry["tflops"] / M.PEAK_BF16_TFLOPS, 4)
+            entry["frac_peak"] = round(entry["tflops"] / peak, 4)
         else:   # the preprocess streams out and dout once and writes delta
             nbytes = 2 * q.numel() * q.element_size() + lse.numel() * 4
             entry["gbs"] = round(nbytes / (per[n] * 1e-3) / 1e9, 1)
@@ -455,16 +459,16 @@ def main():
                    "kv_len": w.kv_len, "n_ring": w.n_ring, "ring_rank": w.ring_rank, "causal": w.causal,
                    "q_chunk": w.q_chunk, "k_chunk": w.k_chunk, "bias": w.bias_len > 0,
                    "segments": w.segments},
-        "frac_peak": round(value / M.PEAK_BF16_TFLOPS, 4),
+        "frac_peak": round(value / peak, 4),
         "fwd_tflops": round(fwd_tflops, 2),
-        "fwd_frac_peak": round(fwd_tflops / M.PEAK_BF16_TFLOPS, 4),
+        "fwd_frac_peak": round(fwd_tflops / peak, 4),
         "tokens_per_s": round(w.batch * w.q_len / (ms_step * 1e-3), 1),
         "visible_pairs": pairs * w.heads,
         "executed": executed,
         "clocks_mhz": clocks.summary(),
         "kernels": kernels,
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": M.PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ach / M.PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                      "traffic": measured_traffic(w.name, dom)},
     }
     if not args.no_cpu_baseline:

@@ -152,14 +152,14 @@ size_t workspace_bytes(const Checked& c) {
   return (b + 255) / 256 * 256;
 }
 
-// bfloat16 runs on the MFMA kernels; float32 keeps float32 products throughout (scalar kernels)
+// bfloat16 runs on the bf16 MFMA kernels; float32 keeps float32 products throughout (float32 MFMA)
 int do_bwd_dkdv(const Checked& c, hipStream_t st) {
-  return hip_status(c.p.bf16 ? ra::launch_bwd_dkdv_mfma(c.p, st) : ra::launch_bwd_dkdv_simt(c.p, st),
+  return hip_status(c.p.bf16 ? ra::launch_bwd_dkdv_mfma(c.p, st) : ra::launch_bwd_dkdv_f32(c.p, st),
                     "dK/dV launch");
 }
 
 int do_bwd_dq(const Checked& c, hipStream_t st) {
-  return hip_status(c.p.bf16 ? ra::launch_bwd_dq_mfma(c.p, st) : ra::launch_bwd_dq_simt(c.p, st), "dQ launch");
+  return hip_status(c.p.bf16 ? ra::launch_bwd_dq_mfma(c.p, st) : ra::launch_bwd_dq_f32(c.p, st), "dQ launch");
 }
 
 }  // namespace
@@ -256,7 +256,7 @@ int ra_blockwise_attn_fwd(const void* q, const void* k, const void* v, const flo
   c.p.lse = lse;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (c.p.bf16) return hip_status(ra::launch_fwd_mfma(c.p, st), "forward launch");
-  return hip_status(ra::launch_fwd_simt(c.p, st), "forward launch");
+  return hip_status(ra::launch_fwd_f32(c.p, st), "forward launch");
 }
 
 size_t ra_blockwise_attn_bwd_workspace_size(const ra_shape* shape, int32_t n_ring) {

@@ -185,10 +185,10 @@ hipError_t launch_fwd_mfma(const Params& p, hipStream_t st);
 hipError_t launch_fwd_step_mfma(const Params& p, hipStream_t st);
 hipError_t launch_fwd_finalize(const Params& p, hipStream_t st);
 hipError_t launch_merge(const Params& p, const void* out_b, const float* lse_b, hipStream_t st);
-hipError_t launch_fwd_simt(const Params& p, hipStream_t st);
+hipError_t launch_fwd_f32(const Params& p, hipStream_t st);
 hipError_t launch_bwd_preprocess(const Params& p, hipStream_t st);
-hipError_t launch_bwd_dkdv_simt(const Params& p, hipStream_t st);
-hipError_t launch_bwd_dq_simt(const Params& p, hipStream_t st);
+hipError_t launch_bwd_dkdv_f32(const Params& p, hipStream_t st);
+hipError_t launch_bwd_dq_f32(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dkdv_mfma(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dkdv_step_mfma(const Params& p, hipStream_t st);

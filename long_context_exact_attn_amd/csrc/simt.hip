@@ -1,112 +1,10 @@
-// Scalar (one lane per query or per key) kernels of libra_attn:
-//  * the float32 forward -- the exact-arithmetic path: float32 products and
-//    float32 probabilities, no bfloat16 rounding anywhere;
-//  * the backward preprocess Delta = rowsum(dO * O) for both dtypes;
-//  * float32 backward dK/dV and dQ kernels.
-// They follow the same ring walks as the MFMA kernels.
+// One-lane-per-row kernels of libra_attn, for both dtypes: the backward preprocess
+// Delta = rowsum(dO * O), the ring-step finalize and merge, the float32-to-output conversion of
+// gradient sums, and the fixed-order reductions that form the bias gradient from per-key sums.
 #include "ra_common.cuh"
 
 namespace ra {
 namespace {
-
-constexpr int kLanes = 64;   // one wavefront per workgroup
-constexpr int BKS = 16;      // keys per LDS tile (forward / dQ)
-constexpr int BQS = 16;      // queries per LDS tile (dK/dV)
-
-template <typename T>
-__device__ __forceinline__ void load_row(float* dst, const T* src, int D) {
-  for (int d = 0; d < D; ++d) dst[d] = to_f32(src[d]);
-}
-
-// ------------------------------------------------------------------ forward (float32)
-template <int D, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
-__global__ __launch_bounds__(kLanes) void fwd_simt_kernel(Params p) {
-  __shared__ float sK[BKS][D];
-  __shared__ float sV[BKS][D];
-  __shared__ float sB[BKS];
-  __shared__ int sS[BKS];
-  const int tid = threadIdx.x;
-  const int HB = p.B * p.H;
-  const int64_t n_qt_blk = (p.Lb + kLanes - 1) / kLanes;
-  const int64_t n_qt = (p.ring_rank < 0 ? p.n_ring : 1) * n_qt_blk;
-  const int64_t wg = blockIdx.x;
-  const int hb = static_cast<int>(wg % HB);
-  const int64_t t = n_qt - 1 - wg / HB;
-  const int b = hb / p.H, h = hb % p.H;
-  const int r_local = static_cast<int>(t / n_qt_blk);
-  const int64_t qa = (t % n_qt_blk) * kLanes;
-  const int r = p.ring_rank < 0 ? r_local : p.ring_rank;
-  const int64_t qrow_base = static_cast<int64_t>(r_local) * p.Lb;
-  const int64_t pos0 = static_cast<int64_t>(r) * p.Lb + qa;
-  const int64_t nrows = (p.Lb - qa) < kLanes ? (p.Lb - qa) : kLanes;
-  const bool valid = tid < nrows;
-  const int64_t qpos = pos0 + tid;
-  const float* qp = static_cast<const float*>(p.q);
-  const float* kp = static_cast<const float*>(p.k);
-  const float* vp = static_cast<const float*>(p.v);
-
-  float qr[D], o[D];
-  const int64_t qoff = row_offset(b, qrow_base + (valid ? qa + tid : 0), h, p.Lq, p.H, D);
-  for (int d = 0; d < D; ++d) { qr[d] = valid ? qp[qoff + d] : 0.f; o[d] = 0.f; }
-  const int qseg = (HAS_SEG && valid) ? p.seg[static_cast<int64_t>(b) * p.Lk + qpos] : 0;
-  const float c = p.scale * kLog2e;
-  float m = -INFINITY, l = 0.f;
-
-  RingWalk walk;
-  walk.begin(p.n_ring, r, p.Lb, CAUSAL,
-             CAUSAL && nrows > 0 ? causal_last_key(static_cast<int>(pos0 + nrows - 1), 0, p.causal) : pos0 + nrows - 1);
-  const int64_t qlim = CAUSAL ? causal_last_key(static_cast<int>(qpos), 0, p.causal) : qpos;   // last visible key
-  while (nrows > 0 && walk.next<BKS>()) {
-    const int64_t key0 = walk.key0, kend = walk.kend;
-    __syncthreads();
-    for (int e = tid; e < BKS * D; e += kLanes) {
-      const int j = e / D, d = e % D;
-      const int64_t key = key0 + j;
-      const bool ok = key < kend;
-      const int64_t off = row_offset(b, ok ? key : 0, h, p.Lk, p.H, D) + d;
-      sK[j][d] = ok ? kp[off] : 0.f;
-      sV[j][d] = ok ? vp[off] : 0.f;
-    }
-    if (tid < BKS) {
-      const int64_t key = key0 + tid;
-      if (HAS_BIAS) sB[tid] = key < kend ? p.bias[h * p.bias_len + key % p.bias_len] * kLog2e : 0.f;
-      if (HAS_SEG) sS[tid] = key < kend ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
-    }
-    __syncthreads();
-    if (!valid) continue;
-    float s[BKS];
-    float mx = -INFINITY;
-    for (int j = 0; j < BKS; ++j) {
-      const int64_t key = key0 + j;
-      bool vis = key < kend;
-      if (CAUSAL) vis = vis && key <= qlim;
-      if (HAS_SEG) vis = vis && sS[j] == qseg;
-      float acc = 0.f;
-      for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qr[d], sK[j][d], acc);
-      float x = acc * c;
-      if (HAS_BIAS) x += sB[j];
-      s[j] = vis ? x : -INFINITY;
-      mx = fmaxf(mx, s[j]);
-    }
-    const float mnew = fmaxf(m, mx);
-    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
-    const float msub = mnew == -INFINITY ? 0.f : mnew;
-    l *= alpha;
-    for (int d = 0; d < D; ++d) o[d] *= alpha;
-    for (int j = 0; j < BKS; ++j) {
-      const float pj = __builtin_amdgcn_exp2f(s[j] - msub);
-      l += pj;
-      for (int d = 0; d < D; ++d) o[d] = __builtin_fmaf(pj, sV[j][d], o[d]);
-    }
-    m = mnew;
-  }
-  if (!valid) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* op = static_cast<float*>(p.out) + qoff;
-  for (int d = 0; d < D; ++d) op[d] = o[d] * inv;
-  p.lse[(static_cast<int64_t>(b) * p.H + h) * p.Lq + qrow_base + qa + tid] =
-      l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
-}
 
 // ------------------------------------------------------------------ backward preprocess
 // delta[b, h, i] = sum_d dout[b, i, h, d] * out[b, i, h, d]; one lane per row.
@@ -194,241 +92,7 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p, const T* out_b, co
   p.lse[si] = lse;
 }
 
-// ------------------------------------------------------------------ backward dK/dV (one lane per key)
-template <typename T, int D, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
-__global__ __launch_bounds__(kLanes) void dkdv_simt_kernel(Params p) {
-  __shared__ float sQ[BQS][D];
-  __shared__ float sG[BQS][D];
-  __shared__ float sL[BQS];
-  __shared__ float sD[BQS];
-  __shared__ int sS[BQS];
-  __shared__ int64_t sP[BQS];
-  const int tid = threadIdx.x;
-  const int HB = p.B * p.H;
-  const int64_t n_kt_blk = (p.Lb + kLanes - 1) / kLanes;
-  const int64_t wg = blockIdx.x;
-  const int hb = static_cast<int>(wg % HB);
-  const int64_t kt = wg / HB;
-  const int b = hb / p.H, h = hb % p.H;
-  const int j = static_cast<int>(kt / n_kt_blk);
-  const int64_t ka = (kt % n_kt_blk) * kLanes;
-  const int64_t kfirst = static_cast<int64_t>(j) * p.Lb + ka;
-  const bool valid = ka + tid < p.Lb;
-  const int64_t key = kfirst + tid;
-  const T* qp = static_cast<const T*>(p.q);
-  const T* kp = static_cast<const T*>(p.k);
-  const T* vp = static_cast<const T*>(p.v);
-  const T* gp = static_cast<const T*>(p.dout);
-
-  float kr[D], vr[D], dk[D], dv[D];
-  const int64_t koff = row_offset(b, valid ? key : 0, h, p.Lk, p.H, D);
-  for (int d = 0; d < D; ++d) {
-    kr[d] = valid ? to_f32(kp[koff + d]) : 0.f;
-    vr[d] = valid ? to_f32(vp[koff + d]) : 0.f;
-    dk[d] = 0.f;
-    dv[d] = 0.f;
-  }
-  const int kseg = (HAS_SEG && valid) ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
-  const float bias_l2 = (HAS_BIAS && valid) ? p.bias[h * p.bias_len + key % p.bias_len] * kLog2e : 0.f;
-  const float c = p.scale * kLog2e;
-  float dsum = 0.f;   // with a bias: sum_i dS_ij of this key, from which the bias gradient is formed
-
-  QueryWalk walk;
-  // the first query able to see this thread's key, and the first able to see the tile's first key
-  const int64_t kfq = CAUSAL ? causal_first_query(static_cast<int>(key), 0, p.causal) : key;
-  walk.begin(p.n_ring, j, p.Lb, CAUSAL, CAUSAL ? causal_first_query(static_cast<int>(kfirst), 0, p.causal) : kfirst,
-             p.ring_rank);
-  while (walk.next<BQS>()) {
-    const int64_t row0 = walk.row0, rend = walk.rend, pbase = walk.pos_base;
-    __syncthreads();
-    for (int e = tid; e < BQS * D; e += kLanes) {
-      const int i = e / D, d = e % D;
-      const int64_t row = row0 + i;
-      const bool ok = row < rend;
-      const int64_t off = row_offset(b, ok ? row : 0, h, p.Lq, p.H, D) + d;
-      sQ[i][d] = ok ? to_f32(qp[off]) : 0.f;
-      sG[i][d] = ok ? to_f32(gp[off]) : 0.f;
-    }
-    if (tid < BQS) {
-      const int64_t row = row0 + tid;
-      const bool ok = row < rend;
-      const int64_t li = (static_cast<int64_t>(b) * p.H + h) * p.Lq + (ok ? row : 0);
-      sL[tid] = ok ? p.lse[li] * kLog2e : INFINITY;
-      sD[tid] = ok ? p.delta[li] : 0.f;
-      sP[tid] = ok ? row + pbase : -1;
-      if (HAS_SEG) sS[tid] = ok ? p.seg[static_cast<int64_t>(b) * p.Lk + row + pbase] : 0;
-    }
-    __syncthreads();
-    if (!valid) continue;
-    for (int i = 0; i < BQS; ++i) {
-      const int64_t qpos = sP[i];
-      bool vis = qpos >= 0;
-      if (CAUSAL) vis = vis && qpos >= kfq;
-      if (HAS_SEG) vis = vis && sS[i] == kseg;
-      if (!vis) continue;
-      float s = 0.f, dp = 0.f;
-      for (int d = 0; d < D; ++d) {
-        s = __builtin_fmaf(sQ[i][d], kr[d], s);
-        dp = __builtin_fmaf(sG[i][d], vr[d], dp);
-      }
-      const float pr = __builtin_amdgcn_exp2f(s * c + bias_l2 - sL[i]);
-      const float ds0 = pr * (dp - sD[i]);
-      if (HAS_BIAS) dsum += ds0;
-      const float ds = ds0 * p.scale;
-      for (int d = 0; d < D; ++d) {
-        dv[d] = __builtin_fmaf(pr, sG[i][d], dv[d]);
-        dk[d] = __builtin_fmaf(ds, sQ[i][d], dk[d]);
-      }
-    }
-  }
-  if (!valid) return;
-  if (HAS_BIAS && p.dbias_keys) p.dbias_keys[(static_cast<int64_t>(b) * p.H + h) * p.Lk + key] = dsum;
-  T* dkp = static_cast<T*>(p.dk) + koff;
-  T* dvp = static_cast<T*>(p.dv) + koff;
-  for (int d = 0; d < D; ++d) {
-    dkp[d] = from_f32<T>(dk[d]);
-    dvp[d] = from_f32<T>(dv[d]);
-  }
-}
-
-// ------------------------------------------------------------------ backward dQ (one lane per query)
-template <typename T, int D, bool CAUSAL, bool HAS_BIAS, bool HAS_SEG>
-__global__ __launch_bounds__(kLanes) void dq_simt_kernel(Params p) {
-  __shared__ float sK[BKS][D];
-  __shared__ float sV[BKS][D];
-  __shared__ float sB[BKS];
-  __shared__ int sS[BKS];
-  const int tid = threadIdx.x;
-  const int HB = p.B * p.H;
-  const int64_t n_qt_blk = (p.Lb + kLanes - 1) / kLanes;
-  const int64_t n_qt = (p.ring_rank < 0 ? p.n_ring : 1) * n_qt_blk;
-  const int64_t wg = blockIdx.x;
-  const int hb = static_cast<int>(wg % HB);
-  const int64_t t = n_qt - 1 - wg / HB;
-  const int b = hb / p.H, h = hb % p.H;
-  const int r_local = static_cast<int>(t / n_qt_blk);
-  const int64_t qa = (t % n_qt_blk) * kLanes;
-  const int r = p.ring_rank < 0 ? r_local : p.ring_rank;
-  const int64_t qrow_base = static_cast<int64_t>(r_local) * p.Lb;
-  const int64_t pos0 = static_cast<int64_t>(r) * p.Lb + qa;
-  const int64_t nrows = (p.Lb - qa) < kLanes ? (p.Lb - qa) : kLanes;
-  const bool valid = tid < nrows;
-  const int64_t qpos = pos0 + tid;
-  const T* qp = static_cast<const T*>(p.q);
-  const T* kp = static_cast<const T*>(p.k);
-  const T* vp = static_cast<const T*>(p.v);
-  const T* gp = static_cast<const T*>(p.dout);
-
-  float qr[D], g[D], dq[D];
-  const int64_t qoff = row_offset(b, qrow_base + (valid ? qa + tid : 0), h, p.Lq, p.H, D);
-  for (int d = 0; d < D; ++d) {
-    qr[d] = valid ? to_f32(qp[qoff + d]) : 0.f;
-    g[d] = valid ? to_f32(gp[qoff + d]) : 0.f;
-    dq[d] = 0.f;
-  }
-  const int64_t li = (static_cast<int64_t>(b) * p.H + h) * p.Lq + qrow_base + (valid ? qa + tid : 0);
-  const float lse_l2 = p.lse[li] * kLog2e;
-  const float delta = p.delta[li];
-  const int qseg = (HAS_SEG && valid) ? p.seg[static_cast<int64_t>(b) * p.Lk + qpos] : 0;
-  const float c = p.scale * kLog2e;
-
-  RingWalk walk;
-  walk.begin(p.n_ring, r, p.Lb, CAUSAL,
-             CAUSAL && nrows > 0 ? causal_last_key(static_cast<int>(pos0 + nrows - 1), 0, p.causal) : pos0 + nrows - 1);
-  const int64_t qlim = CAUSAL ? causal_last_key(static_cast<int>(qpos), 0, p.causal) : qpos;   // last visible key
-  while (nrows > 0 && walk.next<BKS>()) {
-    const int64_t key0 = walk.key0, kend = walk.kend;
-    __syncthreads();
-    for (int e = tid; e < BKS * D; e += kLanes) {
-      const int j = e / D, d = e % D;
-      const int64_t key = key0 + j;
-      const bool ok = key < kend;
-      const int64_t off = row_offset(b, ok ? key : 0, h, p.Lk, p.H, D) + d;
-      sK[j][d] = ok ? to_f32(kp[off]) : 0.f;
-      sV[j][d] = ok ? to_f32(vp[off]) : 0.f;
-    }
-    if (tid < BKS) {
-      const int64_t key = key0 + tid;
-      if (HAS_BIAS) sB[tid] = key < kend ? p.bias[h * p.bias_len + key % p.bias_len] * kLog2e : 0.f;
-      if (HAS_SEG) sS[tid] = key < kend ? p.seg[static_cast<int64_t>(b) * p.Lk + key] : 0;
-    }
-    __syncthreads();
-    if (!valid) continue;
-    for (int j = 0; j < BKS; ++j) {
-      const int64_t key = key0 + j;
-      bool vis = key < kend;
-      if (CAUSAL) vis = vis && key <= qlim;
-      if (HAS_SEG) vis = vis && sS[j] == qseg;
-      if (!vis) continue;
-      float s = 0.f, dp = 0.f;
-      for (int d = 0; d < D; ++d) {
-        s = __builtin_fmaf(qr[d], sK[j][d], s);
-        dp = __builtin_fmaf(g[d], sV[j][d], dp);
-      }
-      float x = s * c;
-      if (HAS_BIAS) x += sB[j];
-      const float pr = __builtin_amdgcn_exp2f(x - lse_l2);
-      const float ds = pr * (dp - delta) * p.scale;
-      for (int d = 0; d < D; ++d) dq[d] = __builtin_fmaf(ds, sK[j][d], dq[d]);
-    }
-  }
-  if (!valid) return;
-  T* dqp = static_cast<T*>(p.dq) + qoff;
-  for (int d = 0; d < D; ++d) dqp[d] = from_f32<T>(dq[d]);
-}
-
-// ------------------------------------------------------------------ launchers
-int64_t q_tiles(const Params& p, int bq) { return (p.ring_rank < 0 ? p.n_ring : 1) * ((p.Lb + bq - 1) / bq); }
-
-#define RA_SELECT_FLAGS(CALL)                                                      \
-  do {                                                                             \
-    const bool c_ = p.causal != 0, b_ = p.bias != nullptr, s_ = p.seg != nullptr;  \
-    if (c_) {                                                                      \
-      if (b_) { if (s_) CALL(true, true, true); else CALL(true, true, false); }    \
-      else { if (s_) CALL(true, false, true); else CALL(true, false, false); }     \
-    } else {                                                                       \
-      if (b_) { if (s_) CALL(false, true, true); else CALL(false, true, false); }  \
-      else { if (s_) CALL(false, false, true); else CALL(false, false, false); }   \
-    }                                                                              \
-  } while (0)
-
-template <int D>
-hipError_t fwd_simt_d(const Params& p, hipStream_t st) {
-  const int64_t grid = q_tiles(p, kLanes) * p.B * p.H;
-  if (grid == 0) return hipSuccess;
-#define RA_L(C, B, S) hipLaunchKernelGGL((fwd_simt_kernel<D, C, B, S>), dim3(grid), dim3(kLanes), 0, st, p)
-  RA_SELECT_FLAGS(RA_L);
-#undef RA_L
-  return hipGetLastError();
-}
-
-template <typename T, int D>
-hipError_t dkdv_simt_d(const Params& p, hipStream_t st) {
-  const int64_t grid = static_cast<int64_t>(p.n_ring) * ((p.Lb + kLanes - 1) / kLanes) * p.B * p.H;
-  if (grid == 0) return hipSuccess;
-#define RA_L(C, B, S) hipLaunchKernelGGL((dkdv_simt_kernel<T, D, C, B, S>), dim3(grid), dim3(kLanes), 0, st, p)
-  RA_SELECT_FLAGS(RA_L);
-#undef RA_L
-  return hipGetLastError();
-}
-
-template <typename T, int D>
-hipError_t dq_simt_d(const Params& p, hipStream_t st) {
-  const int64_t grid = q_tiles(p, kLanes) * p.B * p.H;
-  if (grid == 0) return hipSuccess;
-#define RA_L(C, B, S) hipLaunchKernelGGL((dq_simt_kernel<T, D, C, B, S>), dim3(grid), dim3(kLanes), 0, st, p)
-  RA_SELECT_FLAGS(RA_L);
-#undef RA_L
-  return hipGetLastError();
-}
-
 }  // namespace
-
-hipError_t launch_fwd_simt(const Params& p, hipStream_t st) {
-  if (p.D == 64) return fwd_simt_d<64>(p, st);
-  if (p.D == 128) return fwd_simt_d<128>(p, st);
-  return hipErrorInvalidValue;
-}
 
 template <typename T>
 hipError_t launch_bwd_preprocess_t(const Params& p, hipStream_t st) {
@@ -442,18 +106,6 @@ hipError_t launch_bwd_preprocess_t(const Params& p, hipStream_t st) {
 }
 
 
-template <typename T>
-hipError_t launch_bwd_dkdv_simt_t(const Params& p, hipStream_t st) {
-  if (p.D == 64) return dkdv_simt_d<T, 64>(p, st);
-  if (p.D == 128) return dkdv_simt_d<T, 128>(p, st);
-  return hipErrorInvalidValue;
-}
-template <typename T>
-hipError_t launch_bwd_dq_simt_t(const Params& p, hipStream_t st) {
-  if (p.D == 64) return dq_simt_d<T, 64>(p, st);
-  if (p.D == 128) return dq_simt_d<T, 128>(p, st);
-  return hipErrorInvalidValue;
-}
 template <typename T>
 hipError_t launch_finalize_t(const Params& p, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(p.B) * p.Lq * p.H;
@@ -559,11 +211,4 @@ hipError_t launch_merge(const Params& p, const void* out_b, const float* lse_b, 
 hipError_t launch_bwd_preprocess(const Params& p, hipStream_t st) {
   return p.bf16 ? launch_bwd_preprocess_t<__bf16>(p, st) : launch_bwd_preprocess_t<float>(p, st);
 }
-hipError_t launch_bwd_dkdv_simt(const Params& p, hipStream_t st) {
-  return p.bf16 ? launch_bwd_dkdv_simt_t<__bf16>(p, st) : launch_bwd_dkdv_simt_t<float>(p, st);
-}
-hipError_t launch_bwd_dq_simt(const Params& p, hipStream_t st) {
-  return p.bf16 ? launch_bwd_dq_simt_t<__bf16>(p, st) : launch_bwd_dq_simt_t<float>(p, st);
-}
-
 }  // namespace ra

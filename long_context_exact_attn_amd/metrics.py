@@ -65,5 +65,5 @@ def executed_pairs_per_head(q_first, q_len, kv_len, causal, tile_q, tile_k):
 
 # MI355X published peaks
 PEAK_BF16_TFLOPS = 2500.0     # dense bf16 MFMA
-PEAK_F32_TFLOPS = 157.3       # fp32 vector
+PEAK_F32_TFLOPS = 157.3       # dense fp32, matrix unit and vector unit alike
 PEAK_HBM_GBS = 8000.0
