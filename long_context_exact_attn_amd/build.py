@@ -77,5 +77,68 @@ def build(verbose=False, jobs=None):
     return LIB
 
 
+# ---------------------------------------------------------------- host-sanitized build
+# The C-ABI layer (argument validation, workspace sizing, the static-scratch lookup) with its host code
+# under AddressSanitizer and UndefinedBehaviorSanitizer, linked with the ordinary kernel objects into a
+# second library.  Device code is never instrumented: every sanitizer flag is scoped to the host pass.
+SAN_BUILD = os.path.join(PKG, "_build_san")
+SAN_LIB = os.path.join(PKG, "libra_attn_san.so")
+SANITIZED = ("ra_api.hip", "noalloc.hip")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def _clang():
+    exe = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang++")
+    exe = os.path.normpath(exe)
+    return exe if os.path.exists(exe) else "/opt/rocm/llvm/bin/clang++"
+
+
+def asan_runtime():
+    """Path of the shared AddressSanitizer runtime a host program must preload to load SAN_LIB."""
+    r = subprocess.run([_clang(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found next to the ROCm clang")
+    return path
+
+
+def build_sanitized(verbose=False):
+    """Link libra_attn_san.so: SANITIZED compiled with host sanitizers, every other source as in build()
+    (built first when its objects are missing or older than their sources).  Returns the library path."""
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    headers = glob.glob(os.path.join(CSRC, "*.cuh")) + [os.path.join(ROOT, "include", "ra_attn.h")]
+    newest_header = max(os.path.getmtime(h) for h in headers)
+    plain = [s for s in sources if os.path.basename(s) not in SANITIZED]
+
+    def stale(obj, src):
+        return not os.path.exists(obj) or os.path.getmtime(obj) < max(os.path.getmtime(src), newest_header)
+
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in plain]
+    if any(stale(o, s) for o, s in zip(objs, plain)):
+        build(verbose)
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    for name in SANITIZED:
+        src = os.path.join(CSRC, name)
+        obj = os.path.join(SAN_BUILD, name + ".o")
+        cmd = [hipcc(), *common_flags(), *SAN_FLAGS, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitized compile failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+        objs.append(obj)
+    rocm_lib = os.path.normpath(os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib"))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [_clang(), "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libasan", *objs,
+           "-L", rocm_lib, "-lamdhip64", "-Wl,-rpath," + rocm_lib, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized(verbose=True))
+    else:
+        print(build(verbose=True))
