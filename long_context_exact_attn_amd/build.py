@@ -3,8 +3,9 @@
 Every HIP source under csrc/ is compiled to an object in _build/ and the
 objects are linked into long_context_exact_attn_amd/libra_attn.so.  The
 issue-rate microbenchmark (microbench/rates.hip) is built as a standalone
-program next to its source.  Packed fp32 VALU instructions are disabled for
-all device code.
+program next to its source.  The library links the roctx marker library of
+ROCm's profiler SDK (one named range per entry-point call).  Packed fp32
+VALU instructions are disabled for all device code.
 """
 import concurrent.futures as cf
 import glob
@@ -26,6 +27,10 @@ def hipcc():
     if not os.path.exists(exe):
         raise RuntimeError("hipcc not found (ROCm is required to build libra_attn)")
     return exe
+
+
+def rocm_lib():
+    return os.path.normpath(os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib"))
 
 
 def common_flags():
@@ -69,7 +74,8 @@ def build(verbose=False, jobs=None):
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), sources))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-L", rocm_lib(), "-lrocprofiler-sdk-roctx",
+           "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
@@ -126,10 +132,9 @@ def build_sanitized(verbose=False):
         if r.returncode != 0:
             raise RuntimeError(f"sanitized compile failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
         objs.append(obj)
-    rocm_lib = os.path.normpath(os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib"))
     tmp = SAN_LIB + ".tmp"
     cmd = [_clang(), "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libasan", *objs,
-           "-L", rocm_lib, "-lamdhip64", "-Wl,-rpath," + rocm_lib, "-o", tmp]
+           "-L", rocm_lib(), "-lamdhip64", "-lrocprofiler-sdk-roctx", "-Wl,-rpath," + rocm_lib(), "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"sanitized link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")

@@ -5,6 +5,8 @@
 #include <cstdio>
 #include <string>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "../../include/ra_attn.h"
 #include "ra_common.cuh"
 
@@ -34,6 +36,25 @@ int ok() {
     const int rc_ = (x);       \
     if (rc_ != RA_OK) return rc_; \
   } while (0)
+
+// One roctx range per call of an entry point, from entry to return: it spans the validation and the
+// enqueue on the host, not the kernels' run.  Under a profiler's marker trace each ring step (one
+// _fwd_step or _bwd_step call) and each whole-ring call shows as one named range beside the kernels
+// it launched.  Names use the scalar arguments only, which are valid before validation.
+class Range {
+ public:
+  explicit Range(const char* fmt, ...) {
+    char buf[160];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    roctxRangePushA(buf);
+  }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -188,6 +209,7 @@ size_t ra_blockwise_ffn_workspace_size(int64_t tokens, int32_t d_model, int32_t 
 int ra_blockwise_ffn_fwd(const void* x, const void* w1, const void* w3, const void* w2, void* out, int64_t tokens,
                          int32_t d_model, int32_t d_ff, int64_t chunk, void* workspace, size_t workspace_bytes,
                          void* stream) {
+  Range range("ra_blockwise_ffn_fwd tokens=%lld chunk=%lld", (long long)tokens, (long long)chunk);
   RA_TRY(ffn_check(tokens, d_model, d_ff, chunk));
   const int64_t xe = tokens * d_model, we = static_cast<int64_t>(d_ff) * d_model;
   RA_TRY(need_ptr(x, xe, "x", 2));
@@ -211,6 +233,7 @@ int ra_blockwise_ffn_fwd(const void* x, const void* w1, const void* w3, const vo
 int ra_blockwise_ffn_bwd(const void* x, const void* w1, const void* w3, const void* w2, const void* dout, void* dx,
                          float* dw1, float* dw3, float* dw2, int64_t tokens, int32_t d_model, int32_t d_ff,
                          int64_t chunk, void* workspace, size_t workspace_bytes, void* stream) {
+  Range range("ra_blockwise_ffn_bwd tokens=%lld chunk=%lld", (long long)tokens, (long long)chunk);
   RA_TRY(ffn_check(tokens, d_model, d_ff, chunk));
   const int64_t xe = tokens * d_model, we = static_cast<int64_t>(d_ff) * d_model;
   RA_TRY(need_ptr(x, xe, "x", 2));
@@ -240,6 +263,7 @@ const char* ra_last_error(void) { return g_last_error.c_str(); }
 int ra_blockwise_attn_fwd(const void* q, const void* k, const void* v, const float* bias,
                           const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
                           int32_t causal, void* out, float* lse, const ra_shape* shape, void* stream) {
+  Range range("ra_blockwise_attn_fwd n_ring=%d causal=%d", n_ring, causal);
   Checked c;
   RA_TRY(check_shape(shape, n_ring, &c));
   RA_TRY(check_mask_args(shape, bias, q_chunk, k_chunk, causal, &c));
@@ -273,6 +297,7 @@ size_t ra_blockwise_attn_bwd_dbias_workspace_size(const ra_shape* shape) {
 
 int ra_blockwise_attn_bwd_preprocess(const void* out, const void* dout, float* delta, const ra_shape* shape,
                                      void* stream) {
+  Range range("ra_blockwise_attn_bwd_preprocess");
   RA_TRY(check_dims(shape));
   Checked c;
   c.p = ra::Params{};
@@ -316,6 +341,7 @@ int ra_blockwise_attn_bwd_dkdv(const void* q, const void* k, const void* v, cons
                                const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
                                int32_t causal, const float* lse, const float* delta, const void* dout,
                                void* dk, void* dv, const ra_shape* shape, void* stream) {
+  Range range("ra_blockwise_attn_bwd_dkdv n_ring=%d causal=%d", n_ring, causal);
   Checked c;
   RA_TRY(bwd_common(q, k, v, bias, segment_ids, n_ring, q_chunk, k_chunk, causal, lse, dout, shape, &c));
   RA_TRY(need_ptr(delta, c.rows, "delta", 4));
@@ -332,6 +358,7 @@ int ra_blockwise_attn_bwd_dq(const void* q, const void* k, const void* v, const 
                              const int32_t* segment_ids, int32_t n_ring, int64_t q_chunk, int64_t k_chunk,
                              int32_t causal, const float* lse, const float* delta, const void* dout, void* dq,
                              const ra_shape* shape, void* stream) {
+  Range range("ra_blockwise_attn_bwd_dq n_ring=%d causal=%d", n_ring, causal);
   Checked c;
   RA_TRY(bwd_common(q, k, v, bias, segment_ids, n_ring, q_chunk, k_chunk, causal, lse, dout, shape, &c));
   RA_TRY(need_ptr(delta, c.rows, "delta", 4));
@@ -395,6 +422,7 @@ int ra_blockwise_attn_bwd(const void* q, const void* k, const void* v, const flo
                           int32_t causal, const void* out, const float* lse, const void* dout, void* dq,
                           void* dk, void* dv, void* workspace, size_t workspace_bytes_given,
                           const ra_shape* shape, void* stream) {
+  Range range("ra_blockwise_attn_bwd n_ring=%d causal=%d", n_ring, causal);
   return bwd_full(q, k, v, bias, segment_ids, n_ring, q_chunk, k_chunk, causal, out, lse, dout, dq, dk, dv, nullptr,
                   workspace, workspace_bytes_given, shape, stream);
 }
@@ -404,6 +432,7 @@ int ra_blockwise_attn_bwd_dbias(const void* q, const void* k, const void* v, con
                                 int32_t causal, const void* out, const float* lse, const void* dout, void* dq,
                                 void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes_given,
                                 const ra_shape* shape, void* stream) {
+  Range range("ra_blockwise_attn_bwd_dbias n_ring=%d causal=%d", n_ring, causal);
   if (!dbias) return fail(RA_ERR_ARG, "dbias is NULL");
   return bwd_full(q, k, v, bias, segment_ids, n_ring, q_chunk, k_chunk, causal, out, lse, dout, dq, dk, dv, dbias,
                   workspace, workspace_bytes_given, shape, stream);
@@ -413,6 +442,7 @@ int ra_blockwise_attn_fwd_step(const void* q, const void* k, const void* v, cons
                                const int32_t* segment_ids, int64_t seg_len, int64_t q_pos0, int64_t kv_pos0,
                                int32_t causal, float* o_state, float* m_state, float* l_state, int32_t init,
                                const ra_shape* shape, void* stream) {
+  Range range("ring step fwd q_pos0=%lld kv_pos0=%lld", (long long)q_pos0, (long long)kv_pos0);
   RA_TRY(check_dims(shape));
   if (shape->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "ring steps are implemented for RA_BF16 only");
   if (shape->q_len != shape->kv_len)
@@ -458,6 +488,7 @@ int ra_blockwise_attn_bwd_step(const void* q, const void* k, const void* v, cons
                                int32_t causal, const float* lse, const float* delta, const void* dout, float* dq_acc,
                                float* dk_acc, float* dv_acc, float* dbias_acc, int32_t init_dq, int32_t init_dkv,
                                const ra_shape* shape, void* stream) {
+  Range range("ring step bwd q_pos0=%lld kv_pos0=%lld", (long long)q_pos0, (long long)kv_pos0);
   RA_TRY(check_dims(shape));
   if (shape->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "ring steps are implemented for RA_BF16 only");
   if (shape->q_len != shape->kv_len)
@@ -515,6 +546,7 @@ int ra_blockwise_attn_bwd_step(const void* q, const void* k, const void* v, cons
 
 int ra_blockwise_attn_bwd_dbias_reduce(const float* key_sums, int64_t kv_pos0, float* dbias, int32_t accumulate,
                                        const ra_shape* shape, void* stream) {
+  Range range("ra_blockwise_attn_bwd_dbias_reduce kv_pos0=%lld", (long long)kv_pos0);
   RA_TRY(check_dims(shape));
   if (shape->bias_len < 1 || shape->bias_len >= kMaxPos)
     return fail(RA_ERR_ARG, "bias_len %lld must be in [1, 2^30)", (long long)shape->bias_len);
@@ -534,6 +566,7 @@ int ra_blockwise_attn_bwd_dbias_reduce(const float* key_sums, int64_t kv_pos0, f
 
 int ra_blockwise_attn_bwd_finalize(const float* dq_acc, const float* dk_acc, const float* dv_acc, void* dq, void* dk,
                                    void* dv, const ra_shape* shape, void* stream) {
+  Range range("ra_blockwise_attn_bwd_finalize");
   RA_TRY(check_dims(shape));
   const int64_t HB = static_cast<int64_t>(shape->batch) * shape->heads;
   const int64_t q_elems = HB * shape->q_len * shape->head_dim;
@@ -557,6 +590,7 @@ int ra_blockwise_attn_bwd_finalize(const float* dq_acc, const float* dk_acc, con
 
 int ra_blockwise_attn_fwd_finalize(const float* o_state, const float* m_state, const float* l_state, void* out,
                                    float* lse, const ra_shape* shape, void* stream) {
+  Range range("ra_blockwise_attn_fwd_finalize");
   RA_TRY(check_dims(shape));
   Checked c;
   c.p = ra::Params{};
@@ -584,6 +618,7 @@ int ra_blockwise_attn_fwd_finalize(const float* o_state, const float* m_state, c
 
 int ra_attn_merge(void* out_a, float* lse_a, const void* out_b, const float* lse_b, const ra_shape* shape,
                   void* stream) {
+  Range range("ra_attn_merge");
   RA_TRY(check_dims(shape));
   Checked c;
   c.p = ra::Params{};
