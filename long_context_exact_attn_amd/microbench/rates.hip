@@ -27,18 +27,23 @@ __global__ __launch_bounds__(256) void k_mfma(float* out, float seed) {
 template <int OP>
 __global__ __launch_bounds__(256) void k_valu(float* out, float seed) {
   float x[8];
-  for (int i = 0; i < 8; ++i) x[i] = seed * (threadIdx.x + i);
+  _Float16 xh[8];
+  for (int i = 0; i < 8; ++i) {
+    x[i] = seed * (threadIdx.x + i);
+    xh[i] = (_Float16)x[i];
+  }
   bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
   for (int it = 0; it < N; ++it) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (OP == 0) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+      if (OP == 4) xh[i] = __builtin_elementwise_exp2(-xh[i]);
       if (OP == 1) x[i] = __builtin_fmaf(x[i], 0.999f, 0.001f);
       if (OP == 2) { bf16x2 p = {(__bf16)seed, (__bf16)(seed * 2)}; x[i] = __builtin_amdgcn_fdot2_f32_bf16(p, one, x[i], false); }
       if (OP == 3) x[i] = fmaxf(fmaxf(x[i], seed), x[(i + 1) & 7]);
     }
   }
-  float s = 0; for (int i = 0; i < 8; ++i) s += x[i];
+  float s = 0; for (int i = 0; i < 8; ++i) s += x[i] + (float)xh[i];
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 // one wave mixes MFMA chains with exp chains: do the pipes overlap?
@@ -100,8 +105,12 @@ __global__ __launch_bounds__(512) void k_split(float* out, float seed, int n_mfm
 
 // LDS read bandwidth with the attention kernels' operand patterns on a 64-column bf16 tile
 // whose 16-byte chunks are XOR-swizzled by row: MODE 0 reads 16 bytes per lane (row l % 32,
-// chunk 2 kk + l / 32), MODE 1 the two 8-byte transposing reads of one transposed operand.
-// Each wave reads its own rows of a 32 KiB buffer; the loaded words are folded with xor.
+// chunk 2 u + l / 32), MODE 1 the two 8-byte transposing reads of one transposed operand,
+// MODE 2 a broadcast 16-byte read in which each half of the wave reads one address (the
+// per-row statistics of a 32-row block, four rows per read).  The per-lane byte offsets are
+// formed once; each read takes its offset through an empty asm statement, so that the compiler
+// can neither hoist the loads out of the loop nor add address arithmetic to it.  Each wave
+// reads its own 64-row region of a 32 KiB buffer; the loaded words are folded with xor.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 template <int MODE>
 __global__ __launch_bounds__(256) void k_lds(float* out, int n) {
@@ -109,29 +118,53 @@ __global__ __launch_bounds__(256) void k_lds(float* out, int n) {
   for (int i = threadIdx.x; i < 16384; i += 256) buf[i] = (__bf16)(float)(i & 255);
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
+  const int region = w * 4096;   // element offset of the wave's 64 x 64 region (< 16384)
+  int off[4], off2[4];           // byte offsets, per u
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (MODE == 0) {
+      const int row = l32, chunk = (2 * u + hh) & 7;
+      off[u] = 2 * (region + row * 64 + ((chunk ^ (row & 7)) << 3));
+      off2[u] = 0;
+    } else if (MODE == 2) {
+      off[u] = 2 * region + 4 * (8 * u + 4 * hh);
+      off2[u] = 0;
+    } else {
+      const int g = lane >> 4, gi = lane & 15;
+      const int row = (u & 1) * 16 + 4 * hh + (gi >> 2);
+      const int col = (u >> 1) * 32 + 16 * (g & 1) + 4 * (gi & 3);
+      off[u] = 2 * (region + row * 64 + (((col >> 3) ^ (row & 7)) << 3) + (col & 7));
+      off2[u] = 2 * (region + (row + 8) * 64 + (((col >> 3) ^ ((row + 8) & 7)) << 3) + (col & 7));
+    }
+  }
+  const char* base = reinterpret_cast<const char*>(buf);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   unsigned acc = 0;
   for (int it = 0; it < n; ++it) {
+    int o[4] = {off[0], off[1], off[2], off[3]};
+    int o2[4] = {off2[0], off2[1], off2[2], off2[3]};
+    // one statement for all of the iteration's offsets: its four (eight) reads issue back to back
+    asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o2[0]), "+v"(o2[1]), "+v"(o2[2]),
+                 "+v"(o2[3]));
+    if (MODE != 1) {
+      uint4 x[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = ((it * 4 + u) & 15) * 1024 + w * 256;   // (element offset of a 64-row tile region) < 16384
-      const __bf16* tile = buf + (t & 8191);                  // tiles of 64 x 64 start below 8192 + 4096
-      if (MODE == 0) {
-        const int row = l32, chunk = (2 * u + hh) & 7;
-        const uint4 x = *reinterpret_cast<const uint4*>(tile + row * 64 + ((chunk ^ (row & 7)) << 3));
-        acc ^= x.x ^ x.y ^ x.z ^ x.w;
-      } else {
-        const int g = lane >> 4, gi = lane & 15;
-        const int row = (u & 1) * 16 + 4 * hh + (gi >> 2);
-        const int col = (u >> 1) * 32 + 16 * (g & 1) + 4 * (gi & 3);
-        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-        const __bf16* p0 = tile + row * 64 + (((col >> 3) ^ (row & 7)) << 3) + (col & 7);
-        const __bf16* p1 = tile + (row + 8) * 64 + (((col >> 3) ^ ((row + 8) & 7)) << 3) + (col & 7);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
-        acc ^= (unsigned)(unsigned short)lo[0] ^ ((unsigned)(unsigned short)lo[1] << 16) ^ (unsigned)(unsigned short)lo[2] ^
-               ((unsigned)(unsigned short)lo[3] << 16) ^ (unsigned)(unsigned short)hi[0] ^
-               ((unsigned)(unsigned short)hi[1] << 16) ^ (unsigned)(unsigned short)hi[2] ^ ((unsigned)(unsigned short)hi[3] << 16);
+      for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const uint4*>(base + o[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
+    } else {
+      i16x4 lo[4], hi[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        lo[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + o[u]));
+        hi[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + o2[u]));
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        acc ^= (unsigned)(unsigned short)lo[u][0] ^ ((unsigned)(unsigned short)lo[u][1] << 16) ^
+               (unsigned)(unsigned short)lo[u][2] ^ ((unsigned)(unsigned short)lo[u][3] << 16) ^
+               (unsigned)(unsigned short)hi[u][0] ^ ((unsigned)(unsigned short)hi[u][1] << 16) ^
+               (unsigned)(unsigned short)hi[u][2] ^ ((unsigned)(unsigned short)hi[u][3] << 16);
     }
   }
   out[blockIdx.x * blockDim.x + threadIdx.x] = (float)acc;
@@ -176,8 +209,8 @@ int main() {
     printf("mfma32x32x16 wg/CU=%d: %.3f ms %.1f TFLOP/s  cycles/mfma/SIMD(at 2.4GHz)=%.2f\n", wpc, ms, fl / ms / 1e9,
            ms * 1e-3 * 2.4e9 / (double(wpc) * N * 4));
   }
-  const char* names[] = {"v_exp_f32", "v_fma_f32", "v_dot2_f32_bf16", "v_max(2)"};
-  for (int op = 0; op < 4; ++op)
+  const char* names[] = {"v_exp_f32", "v_fma_f32", "v_dot2_f32_bf16", "v_max(2)", "v_exp_f16"};
+  for (int op = 0; op < 5; ++op)
     for (int wpc : {1, 2, 4}) {
       const int g = cus * wpc;
       float ms = timeit([&] {
@@ -185,6 +218,7 @@ int main() {
         if (op == 1) hipLaunchKernelGGL(k_valu<1>, dim3(g), dim3(256), 0, 0, out, 0.5f);
         if (op == 2) hipLaunchKernelGGL(k_valu<2>, dim3(g), dim3(256), 0, 0, out, 0.5f);
         if (op == 3) hipLaunchKernelGGL(k_valu<3>, dim3(g), dim3(256), 0, 0, out, 0.5f);
+        if (op == 4) hipLaunchKernelGGL(k_valu<4>, dim3(g), dim3(256), 0, 0, out, 0.5f);
       });
       double ops = double(g) * 4 * N * 8;   // wave-instructions
       printf("%s wg/CU=%d: %.3f ms  cycles per wave-instr per SIMD (2.4GHz) = %.2f\n", names[op], wpc, ms,
@@ -212,17 +246,19 @@ int main() {
              op == 0 ? "exp" : "fma", N, tm, nv, op == 0 ? "exp" : "fma", tv, tb, tm + tv, tm > tv ? tm : tv);
     }
   }
-  for (int mode = 0; mode < 2; ++mode)
-    for (int wpc : {1, 2}) {   // 4 or 8 waves per CU
+  const char* lds_names[] = {"ds_read_b128", "2x ds_read_b64_tr_b16", "ds_read_b128 broadcast (2 addresses)"};
+  for (int mode = 0; mode < 3; ++mode)
+    for (int wpc : {1, 2, 4}) {   // 4, 8 or 16 waves per CU (32 KiB of LDS per workgroup)
       const int g = cus * wpc;
       const int n = 4096;
       float ms = timeit([&] {
         if (mode == 0) hipLaunchKernelGGL(k_lds<0>, dim3(g), dim3(256), 0, 0, out, n);
-        else hipLaunchKernelGGL(k_lds<1>, dim3(g), dim3(256), 0, 0, out, n);
+        else if (mode == 1) hipLaunchKernelGGL(k_lds<1>, dim3(g), dim3(256), 0, 0, out, n);
+        else hipLaunchKernelGGL(k_lds<2>, dim3(g), dim3(256), 0, 0, out, n);
       });
       const double bytes = double(g) * 4 * n * 4 * 1024;   // every operand read moves 1 KiB per wave
-      printf("lds %s wg/CU=%d: %.3f ms, %.1f bytes/clk/CU at 2.4 GHz\n", mode == 0 ? "ds_read_b128" : "2x ds_read_b64_tr_b16",
-             wpc, ms, bytes / (ms * 1e-3 * 2.4e9) / cus);
+      printf("lds %s wg/CU=%d: %.3f ms, %.1f bytes/clk/CU at 2.4 GHz\n", lds_names[mode], wpc, ms,
+             bytes / (ms * 1e-3 * 2.4e9) / cus);
     }
   CHECK(hipFree(out));
   return 0;
