@@ -47,36 +47,48 @@ struct StoreBf16 {
   __device__ void operator()(const f32x16 (&acc)[4][2], int64_t mb0, int64_t nb0, int, int l32, int hh, int64_t M,
                              int64_t N) const {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t n = nb0 + 32 * b + l32;
-      if (n >= N) continue;
+    for (int a = 0; a < 4; ++a) {
+      const int64_t m = mb0 + 32 * a + l32;
+      if (m >= M) continue;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t m = mb0 + 32 * a + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (m < M) C[m * ldc + n] = (__bf16)acc[a][b][v];
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = nb0 + 32 * b + 8 * g + 4 * hh;   // N is a multiple of 8: n < N covers n + 3
+          if (n >= N) continue;
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (__bf16)acc[a][b][4 * g + e];
+          *reinterpret_cast<bf16x4*>(C + m * ldc + n) = o;
         }
     }
   }
 };
 
-// h = silu(g) u into H [M, f]: block b = 0 of the wave holds g, b = 1 holds u, j = nb0 / 2 + l32
+// h = silu(g) u into H [M, f]: block b = 0 of the wave holds g, b = 1 holds u, of hidden units
+// j = nb0 / 2 + 8 g + 4 hh + e
 struct GateFwd {
   __bf16* H;
   int64_t f;
   __device__ void operator()(const f32x16 (&acc)[4][2], int64_t mb0, int64_t nb0, int, int l32, int hh, int64_t M,
                              int64_t) const {
-    const int64_t j = nb0 / 2 + l32;
-    if (j >= f) return;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 4; ++a) {
+      const int64_t m = mb0 + 32 * a + l32;
+      if (m >= M) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = mb0 + 32 * a + 8 * (v >> 2) + 4 * hh + (v & 3);
-        const float g = acc[a][0][v], u = acc[a][1][v];
-        if (m < M) H[m * f + j] = (__bf16)(g * sigmoidf_(g) * u);
+      for (int g = 0; g < 4; ++g) {
+        const int64_t j = nb0 / 2 + 8 * g + 4 * hh;   // f is a multiple of 8: j < f covers j + 3
+        if (j >= f) continue;
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gv = acc[a][0][4 * g + e], uv = acc[a][1][4 * g + e];
+          o[e] = (__bf16)(gv * sigmoidf_(gv) * uv);
+        }
+        *reinterpret_cast<bf16x4*>(H + m * f + j) = o;
       }
+    }
   }
 };
 
@@ -84,26 +96,33 @@ struct GateFwd {
 // with dh = dout W2 already in DH [M, f] and s = sigmoid(g),
 //   dg = dh u s (1 + g (1 - s)),  du = dh g s   into DGDU [M, 2 f] (g's columns, then u's)
 //   h = g s u                                   into H [M, f]
-// so g and u never leave the registers.  One 32-row block at a time; its dh values are all loaded
-// before any result is stored (the pointers are declared not to alias, so the loads overlap).
-__device__ __forceinline__ void gate_bwd_block(const __bf16* __restrict__ DH, __bf16* __restrict__ DGDU,
-                                               __bf16* __restrict__ H, const f32x16 (&acc)[2], int64_t mrow0,
-                                               int64_t j, int hh, int64_t M, int64_t f) {
-  if (j >= f) return;
-  float dh[16];
+// so g and u never leave the registers.  One row at a time, four hidden units per access; the row's
+// dh values are all loaded before any result is stored (the pointers are declared not to alias, so
+// the loads overlap).
+__device__ __forceinline__ void gate_bwd_row(const __bf16* __restrict__ DH, __bf16* __restrict__ DGDU,
+                                             __bf16* __restrict__ H, const f32x16 (&acc)[2], int64_t m, int64_t j0,
+                                             int64_t f) {
+  bf16x4 dh[4];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t m = mrow0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-    dh[v] = m < M ? (float)DH[m * f + j] : 0.f;
+  for (int g = 0; g < 4; ++g) {
+    const int64_t j = j0 + 8 * g;
+    dh[g] = j < f ? *reinterpret_cast<const bf16x4*>(DH + m * f + j) : bf16x4{};
   }
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t m = mrow0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-    if (m >= M) continue;
-    const float g = acc[0][v], u = acc[1][v], s = sigmoidf_(g);
-    DGDU[m * 2 * f + j] = (__bf16)(dh[v] * u * s * (1.f + g * (1.f - s)));
-    DGDU[m * 2 * f + f + j] = (__bf16)(dh[v] * g * s);
-    H[m * f + j] = (__bf16)(g * s * u);
+  for (int g = 0; g < 4; ++g) {
+    const int64_t j = j0 + 8 * g;
+    if (j >= f) continue;
+    bf16x4 dg, du, h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gv = acc[0][4 * g + e], uv = acc[1][4 * g + e], sv = sigmoidf_(gv), d = (float)dh[g][e];
+      dg[e] = (__bf16)(d * uv * sv * (1.f + gv * (1.f - sv)));
+      du[e] = (__bf16)(d * gv * sv);
+      h[e] = (__bf16)(gv * sv * uv);
+    }
+    *reinterpret_cast<bf16x4*>(DGDU + m * 2 * f + j) = dg;
+    *reinterpret_cast<bf16x4*>(DGDU + m * 2 * f + f + j) = du;
+    *reinterpret_cast<bf16x4*>(H + m * f + j) = h;
   }
 }
 
@@ -115,12 +134,15 @@ struct GateBwd {
   __device__ void operator()(const f32x16 (&acc)[4][2], int64_t mb0, int64_t nb0, int, int l32, int hh, int64_t M,
                              int64_t) const {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) gate_bwd_block(DH, DGDU, H, acc[a], mb0 + 32 * a, nb0 / 2 + l32, hh, M, f);
+    for (int a = 0; a < 4; ++a) {
+      const int64_t m = mb0 + 32 * a + l32;
+      if (m < M) gate_bwd_row(DH, DGDU, H, acc[a], m, nb0 / 2 + 4 * hh, f);
+    }
   }
 };
 
 // float32 result rows [0, rsplit) into out1 and the rest into out2 (row length ldo): written
-// (splits == 1) or as split `split`'s partial sum into part [splits][M][N]
+// (splits == 1) or as split `split`'s partial sum into part [splits][M][N]; four columns per store
 struct F32Out {
   float* out1;
   float* out2;
@@ -131,20 +153,24 @@ struct F32Out {
   __device__ void operator()(const f32x16 (&acc)[4][2], int64_t mb0, int64_t nb0, int split, int l32, int hh,
                              int64_t M, int64_t N) const {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t n = nb0 + 32 * b + l32;
-      if (n >= N) continue;
+    for (int a = 0; a < 4; ++a) {
+      const int64_t m = mb0 + 32 * a + l32;
+      if (m >= M) continue;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t m = mb0 + 32 * a + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (m >= M) continue;
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = nb0 + 32 * b + 8 * g + 4 * hh;   // N is a multiple of 8
+          if (n >= N) continue;
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = acc[a][b][4 * g + e];
           if (splits > 1) {
-            part[(static_cast<int64_t>(split) * M + m) * N + n] = acc[a][b][v];
+            *reinterpret_cast<f32x4*>(part + (static_cast<int64_t>(split) * M + m) * N + n) = x;
           } else {
             float* o = m < rsplit ? out1 + m * ldo + n : out2 + (m - rsplit) * ldo + n;
-            *o = accumulate ? *o + acc[a][b][v] : acc[a][b][v];
+            if (accumulate) x += *reinterpret_cast<const f32x4*>(o);
+            *reinterpret_cast<f32x4*>(o) = x;
           }
         }
     }

@@ -174,7 +174,10 @@ __device__ __forceinline__ void copy_tile(const Operand& o, int64_t k0, int64_t 
 }
 
 // Epilogue interface: epi(acc, mb0, nb0, split, l32, hh, M, N) is called once per wave with its tile,
-//   acc[a][b][v] = C[mb0 + 32 a + 8 (v / 4) + 4 hh + v % 4][nb0 + 32 b + l32]
+//   acc[a][b][4 g + e] = C[mb0 + 32 a + l32][nb0 + 32 b + 8 g + 4 hh + e]    (g, e = 0..3)
+// The products take B's fragment as their first operand, which gives the transposed accumulator
+// layout: each lane holds four consecutive columns of one row, so an epilogue stores four elements
+// per instruction (the operand fragments of a 32 x 32 x 16 product have the same form on both sides).
 // b_valid: the B tile is inside its operand when n0 + BN <= b_valid.
 template <bool A_KMAJ, bool B_KMAJ, typename BRowMap, typename Epi>
 __global__ __launch_bounds__(kThreadsG) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(kThreadsG) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bf[b], acc[a][b]);
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(bf[b], af[a], acc[a][b]);
     }
     // the next tile's copies must have landed before anyone reads them (those issued in this iteration
     // may stay in flight), and every wave must be done with this tile's stage before copies overwrite it

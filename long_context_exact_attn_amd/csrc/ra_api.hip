@@ -212,11 +212,11 @@ int ra_blockwise_ffn_fwd(const void* x, const void* w1, const void* w3, const vo
   Range range("ra_blockwise_ffn_fwd tokens=%lld chunk=%lld", (long long)tokens, (long long)chunk);
   RA_TRY(ffn_check(tokens, d_model, d_ff, chunk));
   const int64_t xe = tokens * d_model, we = static_cast<int64_t>(d_ff) * d_model;
-  RA_TRY(need_ptr(x, xe, "x", 2));
-  RA_TRY(need_ptr(out, xe, "out", 2));
-  RA_TRY(need_ptr(w1, we, "w1", 2));
-  RA_TRY(need_ptr(w3, we, "w3", 2));
-  RA_TRY(need_ptr(w2, we, "w2", 2));
+  RA_TRY(need_ptr(x, xe, "x", 16));
+  RA_TRY(need_ptr(out, xe, "out", 16));
+  RA_TRY(need_ptr(w1, we, "w1", 16));
+  RA_TRY(need_ptr(w3, we, "w3", 16));
+  RA_TRY(need_ptr(w2, we, "w2", 16));
   if (tokens == 0) return ok();
   const size_t need = ra::ffn_workspace(tokens, d_model, d_ff, chunk, false).bytes;
   if (!workspace || workspace_bytes < need)
@@ -236,15 +236,15 @@ int ra_blockwise_ffn_bwd(const void* x, const void* w1, const void* w3, const vo
   Range range("ra_blockwise_ffn_bwd tokens=%lld chunk=%lld", (long long)tokens, (long long)chunk);
   RA_TRY(ffn_check(tokens, d_model, d_ff, chunk));
   const int64_t xe = tokens * d_model, we = static_cast<int64_t>(d_ff) * d_model;
-  RA_TRY(need_ptr(x, xe, "x", 2));
-  RA_TRY(need_ptr(dout, xe, "dout", 2));
-  RA_TRY(need_ptr(dx, xe, "dx", 2));
-  RA_TRY(need_ptr(w1, we, "w1", 2));
-  RA_TRY(need_ptr(w3, we, "w3", 2));
-  RA_TRY(need_ptr(w2, we, "w2", 2));
-  RA_TRY(need_ptr(dw1, we, "dw1", 4));
-  RA_TRY(need_ptr(dw3, we, "dw3", 4));
-  RA_TRY(need_ptr(dw2, we, "dw2", 4));
+  RA_TRY(need_ptr(x, xe, "x", 16));
+  RA_TRY(need_ptr(dout, xe, "dout", 16));
+  RA_TRY(need_ptr(dx, xe, "dx", 16));
+  RA_TRY(need_ptr(w1, we, "w1", 16));
+  RA_TRY(need_ptr(w3, we, "w3", 16));
+  RA_TRY(need_ptr(w2, we, "w2", 16));
+  RA_TRY(need_ptr(dw1, we, "dw1", 16));
+  RA_TRY(need_ptr(dw3, we, "dw3", 16));
+  RA_TRY(need_ptr(dw2, we, "dw2", 16));
   const size_t need = tokens ? ra::ffn_workspace(tokens, d_model, d_ff, chunk, true).bytes : 0;
   if (need && (!workspace || workspace_bytes < need))
     return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
