@@ -198,17 +198,18 @@ __device__ __forceinline__ void wg_id_range(int lo, int hi, int (&s)[NW][2], int
 // tiles costs one coalesced load of 64 ids and one ballot; the result is wave-uniform.
 __device__ __forceinline__ uint64_t seg_window_mask(const int* __restrict__ ids, int start, int end, int lo, int hi,
                                                     int lane) {
+  constexpr int STEP = 32;   // loads issued before their ballots (two round trips per window)
   uint64_t m = 0;
 #pragma unroll
-  for (int g = 0; g < 64; g += 16) {
-    int id[16];
+  for (int g = 0; g < 64; g += STEP) {
+    int id[STEP];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < STEP; ++i) {
       const int q = start + (g + i) * 64 + lane;
       id[i] = q < end ? ids[q] : 0;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < STEP; ++i) {
       const bool inside = start + (g + i) * 64 + lane < end;
       if (__ballot(inside && id[i] >= lo && id[i] <= hi) != 0) m |= uint64_t(1) << (g + i);
     }
