@@ -9,6 +9,7 @@
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int N = 4096;
 
 __global__ __launch_bounds__(256) void k_mfma(float* out, float seed) {
@@ -170,6 +171,59 @@ __global__ __launch_bounds__(256) void k_lds(float* out, int n) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = (float)acc;
 }
 
+// Phase alternation of the attention kernels: each wave runs a matrix phase (32 MFMAs: four
+// accumulators, eight dependent products each) and then a vector phase that depends on it (64
+// exponentials, 64 adds and 32 bf16 packs, whose output is the next matrix phase's operand).
+// One 8-wave workgroup per CU (two waves per SIMD).  MODE 0: free-running; MODE 1: a barrier after
+// every phase with waves 0-3 and 4-7 in the same phase; MODE 2: the same barriers with waves 4-7
+// one phase behind (ping-pong: one wave of each SIMD in its matrix phase while the other is in its
+// vector phase).
+template <int MODE>
+__global__ __launch_bounds__(512) void k_phase(float* out, float seed, int n) {
+  const int wave = threadIdx.x >> 6;
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) { a[i] = (__bf16)(seed * i); b[i] = (__bf16)(seed + i); }
+  f32x16 acc[4];
+  for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
+  float lsum = 0.f;
+  auto mma_phase = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+  };
+  auto vec_phase = [&]() {
+    float part = 0.f;
+    bf16x8 na;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(acc[j][v] * -1e-6f);
+        const float e1 = __builtin_amdgcn_exp2f(acc[j][v + 1] * -1e-6f);
+        part += e0 + e1;
+        const bf16x2 pr = __builtin_convertvector((f32x2){e0, e1}, bf16x2);
+        na[(v >> 1) & 7] = pr[0];   // the last packs of the phase feed the next matrix phase
+      }
+    lsum += part;
+    a = na;
+  };
+  if (MODE == 2 && wave >= 4) {
+    vec_phase();
+    __syncthreads();
+  }
+  for (int it = 0; it < n; ++it) {
+    mma_phase();
+    if (MODE != 0) __syncthreads();
+    vec_phase();
+    if (MODE != 0) __syncthreads();
+  }
+  if (MODE == 2 && wave < 4) __syncthreads();
+  float s2 = lsum;
+  for (int j = 0; j < 4; ++j) for (int v = 0; v < 16; ++v) s2 += acc[j][v];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s2;
+}
+
 #define CHECK(x)                                                                  \
   do {                                                                            \
     hipError_t e_ = (x);                                                          \
@@ -260,6 +314,21 @@ int main() {
       printf("lds %s wg/CU=%d: %.3f ms, %.1f bytes/clk/CU at 2.4 GHz\n", lds_names[mode], wpc, ms,
              bytes / (ms * 1e-3 * 2.4e9) / cus);
     }
+  {
+    const int g = cus, n = 512;   // one 8-wave workgroup per CU
+    const char* phase_names[] = {"free-running", "barriers, in phase", "barriers, ping-pong"};
+    float t[3];
+    for (int mode = 0; mode < 3; ++mode) {
+      t[mode] = timeit([&] {
+        if (mode == 0) hipLaunchKernelGGL(k_phase<0>, dim3(g), dim3(512), 0, 0, out, 0.5f, n);
+        else if (mode == 1) hipLaunchKernelGGL(k_phase<1>, dim3(g), dim3(512), 0, 0, out, 0.5f, n);
+        else hipLaunchKernelGGL(k_phase<2>, dim3(g), dim3(512), 0, 0, out, 0.5f, n);
+      });
+      // MFMA work: 8 waves x n x 32 products per CU
+      const double fl = double(g) * 8 * n * 32 * 32768.0;
+      printf("phases %s: %.3f ms, %.1f TFLOP/s\n", phase_names[mode], t[mode], fl / (t[mode] * 1e-3) / 1e12);
+    }
+  }
   CHECK(hipFree(out));
   return 0;
 }
