@@ -194,14 +194,21 @@ __global__ __launch_bounds__(kThreadsG) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int wm = wave >> 2, wn = wave & 3;
 
   // workgroup -> tile: consecutive workgroups go to different XCDs, so each XCD gets a contiguous
-  // range of tiles (neighbouring tiles share their A panel in that XCD's L2)
+  // range of tiles.  Inside it the tiles go in groups of GM tile rows, the row fastest: the 32
+  // workgroups an XCD runs at once cover about 8 x 4 tiles and share 8 A and 4 B panels in that
+  // XCD's L2 (one tile column at a time would need 32 A panels per k step).
+  constexpr int GM = 8;
   const int total = tiles_m * tiles_n * splits;
   const int w = blockIdx.x, x = w & 7, i = w >> 3;
   const int q = total >> 3, rr = total & 7;
   const int t = x * q + (x < rr ? x : rr) + i;
   const int split = t / (tiles_m * tiles_n);
   const int tt = t % (tiles_m * tiles_n);
-  const int tm = tt % tiles_m, tn = tt / tiles_m;
+  const int group = tt / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gm = tiles_m - first_m < GM ? tiles_m - first_m : GM;   // rows in this (possibly last) group
+  const int rg = tt - group * GM * tiles_n;
+  const int tm = first_m + rg % gm, tn = rg / gm;
   const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
   const int64_t kbeg = static_cast<int64_t>(split) * k_per_split;
   const int64_t kend = kbeg + k_per_split < K ? kbeg + k_per_split : K;
