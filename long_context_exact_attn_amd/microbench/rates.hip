@@ -173,24 +173,71 @@ __global__ __launch_bounds__(256) void k_lds(float* out, int n) {
 
 // Phase alternation of the attention kernels: each wave runs a matrix phase (32 MFMAs: four
 // accumulators, eight dependent products each) and then a vector phase that depends on it (64
-// exponentials, 64 adds and 32 bf16 packs, whose output is the next matrix phase's operand).
-// One 8-wave workgroup per CU (two waves per SIMD).  MODE 0: free-running; MODE 1: a barrier after
-// every phase with waves 0-3 and 4-7 in the same phase; MODE 2: the same barriers with waves 4-7
-// one phase behind (ping-pong: one wave of each SIMD in its matrix phase while the other is in its
-// vector phase).
+// exponentials, 64 adds and bf16 packs, whose output is the next matrix phase's operand).  Two
+// waves per SIMD.  MODE 0: one 8-wave workgroup per CU, free-running; MODE 1: a barrier after every
+// phase, waves 0-3 and 4-7 in the same phase; MODE 2: the same barriers with waves 4-7 one phase
+// behind (ping-pong); MODE 3: two 4-wave workgroups per CU, free-running; MODE 4: MODE 3 with one
+// barrier per iteration in each workgroup (as the attention loops have per tile); MODE 5: MODE 4
+// with the matrix phase's A operands read from LDS (seven 16-byte reads per iteration, each feeding
+// four products, as the forward's K fragments do); MODE 6: MODE 5 plus direct global -> LDS copies
+// of 16 KiB per workgroup and iteration (a K and a V tile of 64 x 64 bf16), issued at the start of
+// the iteration and waited for before its barrier, as the forward's loop does.  The source is a
+// 64 MiB buffer; workgroup w reads tile (131 w + it) mod 4096 of it.
 template <int MODE>
-__global__ __launch_bounds__(512) void k_phase(float* out, float seed, int n) {
-  const int wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(512) void k_phase(float* out, float seed, int n, const __bf16* src) {
+  __shared__ __attribute__((aligned(16))) __bf16 sbuf[8192];
+  __shared__ __attribute__((aligned(16))) __bf16 sdst[8192];   // MODE 6: the copies' destination
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (MODE >= 5) {
+    for (int i = threadIdx.x; i < 8192; i += blockDim.x) sbuf[i] = (__bf16)(float)(i & 7);
+    __syncthreads();
+  }
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);
+  auto copies = [&](int it) {
+    // four 1 KiB copies per wave (4 waves x 4 KiB = 16 KiB); byte offset < 4096 * 16 KiB = 64 MiB
+    const int64_t tile = (static_cast<int64_t>(blockIdx.x) * 131 + it) % 4096;
+    const char* g = reinterpret_cast<const char*>(src) + tile * 16384 + uwave * 4096 + lane * 16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const unsigned d = static_cast<unsigned>(
+          reinterpret_cast<size_t>((__attribute__((address_space(3))) void*)(sdst + uwave * 2048 + k * 512)));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   : : "s"(d), "v"(g + k * 1024) : "memory", "m0");
+    }
+  };
   bf16x8 a, b;
   for (int i = 0; i < 8; ++i) { a[i] = (__bf16)(seed * i); b[i] = (__bf16)(seed + i); }
   f32x16 acc[4];
   for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
   float lsum = 0.f;
+  // MODE 5: per-lane byte offsets of eight 16-byte reads (row lane % 32, a swizzled chunk), inside
+  // the wave's own 4 KiB region of sbuf (waves 0-3)
+  int off[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int row = lane & 31, chunk = (2 * (k & 3) + (lane >> 5)) ^ (row & 7);
+    off[k] = 2 * ((wave & 3) * 2048 + row * 64 + chunk * 8);
+  }
+  const char* sb = reinterpret_cast<const char*>(sbuf);
   auto mma_phase = [&]() {
+    if constexpr (MODE >= 5) {
+      int o[8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
+      for (int k = 0; k < 8; ++k) o[k] = off[k];
+      asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]), "+v"(o[5]), "+v"(o[6]), "+v"(o[7]));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+      for (int kk = 0; kk < 8; ++kk) {
+        // step 0 takes the previous vector phase's output, the others an LDS fragment
+        const bf16x8 aa = kk == 0 ? a : *reinterpret_cast<const bf16x8*>(sb + o[kk]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, b, acc[j], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    }
   };
   auto vec_phase = [&]() {
     float part = 0.f;
@@ -213,10 +260,12 @@ __global__ __launch_bounds__(512) void k_phase(float* out, float seed, int n) {
     __syncthreads();
   }
   for (int it = 0; it < n; ++it) {
+    if (MODE == 6) copies(it);
     mma_phase();
-    if (MODE != 0) __syncthreads();
+    if (MODE == 1 || MODE == 2) __syncthreads();
     vec_phase();
-    if (MODE != 0) __syncthreads();
+    if (MODE == 6) __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+    if (MODE != 0 && MODE != 3) __syncthreads();
   }
   if (MODE == 2 && wave < 4) __syncthreads();
   float s2 = lsum;
@@ -316,18 +365,30 @@ int main() {
     }
   {
     const int g = cus, n = 512;   // one 8-wave workgroup per CU
-    const char* phase_names[] = {"free-running", "barriers, in phase", "barriers, ping-pong"};
-    float t[3];
-    for (int mode = 0; mode < 3; ++mode) {
-      t[mode] = timeit([&] {
-        if (mode == 0) hipLaunchKernelGGL(k_phase<0>, dim3(g), dim3(512), 0, 0, out, 0.5f, n);
-        else if (mode == 1) hipLaunchKernelGGL(k_phase<1>, dim3(g), dim3(512), 0, 0, out, 0.5f, n);
-        else hipLaunchKernelGGL(k_phase<2>, dim3(g), dim3(512), 0, 0, out, 0.5f, n);
+    const char* phase_names[] = {"8-wave workgroup, free-running", "8-wave workgroup, barriers, in phase",
+                                 "8-wave workgroup, barriers, ping-pong", "two 4-wave workgroups, free-running",
+                                 "two 4-wave workgroups, a barrier per iteration",
+                                 "two 4-wave workgroups, a barrier per iteration, A operands from LDS",
+                                 "the same plus 16 KiB of direct global -> LDS copies per iteration"};
+    __bf16* src;
+    CHECK(hipMalloc(&src, size_t(64) << 20));
+    CHECK(hipMemset(src, 0, size_t(64) << 20));
+    for (int mode = 0; mode < 7; ++mode) {
+      const int threads = mode >= 3 ? 256 : 512, wgs = mode >= 3 ? 2 * g : g;
+      const float t = timeit([&] {
+        if (mode == 0) hipLaunchKernelGGL(k_phase<0>, dim3(wgs), dim3(threads), 0, 0, out, 0.5f, n, src);
+        else if (mode == 1) hipLaunchKernelGGL(k_phase<1>, dim3(wgs), dim3(threads), 0, 0, out, 0.5f, n, src);
+        else if (mode == 2) hipLaunchKernelGGL(k_phase<2>, dim3(wgs), dim3(threads), 0, 0, out, 0.5f, n, src);
+        else if (mode == 3) hipLaunchKernelGGL(k_phase<3>, dim3(wgs), dim3(threads), 0, 0, out, 0.5f, n, src);
+        else if (mode == 4) hipLaunchKernelGGL(k_phase<4>, dim3(wgs), dim3(threads), 0, 0, out, 0.5f, n, src);
+        else if (mode == 5) hipLaunchKernelGGL(k_phase<5>, dim3(wgs), dim3(threads), 0, 0, out, 0.5f, n, src);
+        else hipLaunchKernelGGL(k_phase<6>, dim3(wgs), dim3(threads), 0, 0, out, 0.5f, n, src);
       });
       // MFMA work: 8 waves x n x 32 products per CU
       const double fl = double(g) * 8 * n * 32 * 32768.0;
-      printf("phases %s: %.3f ms, %.1f TFLOP/s\n", phase_names[mode], t[mode], fl / (t[mode] * 1e-3) / 1e12);
+      printf("phases %s: %.3f ms, %.1f TFLOP/s\n", phase_names[mode], t, fl / (t * 1e-3) / 1e12);
     }
+    CHECK(hipFree(src));
   }
   CHECK(hipFree(out));
   return 0;
