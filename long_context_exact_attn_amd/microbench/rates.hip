@@ -273,6 +273,23 @@ __global__ __launch_bounds__(512) void k_phase(float* out, float seed, int n, co
   out[blockIdx.x * blockDim.x + threadIdx.x] = s2;
 }
 
+// Accumulating into a float32 array with hardware atomics: each workgroup adds 32 KiB tiles (128 rows
+// of 64 floats, the partial dQ a 128-key workgroup would add for one query tile) into a 32 MiB array.
+// MODE 0: workgroup w adds tile (37 w + it) mod T (spread); MODE 1: tile it mod T (every workgroup on
+// the same tile at once); MODE 2: plain stores, spread.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_atomic(float* dst, int T, int iters) {
+  for (int it = 0; it < iters; ++it) {
+    const int t = MODE == 1 ? (it % T) : ((static_cast<int>(blockIdx.x) * 37 + it) % T);
+    float* base = dst + static_cast<size_t>(t) * 8192;   // t < T: inside the T * 8192 floats
+#pragma unroll 4
+    for (int i = threadIdx.x; i < 8192; i += 256) {
+      if (MODE == 2) base[i] = 1.0f;
+      else unsafeAtomicAdd(base + i, 1.0f);
+    }
+  }
+}
+
 #define CHECK(x)                                                                  \
   do {                                                                            \
     hipError_t e_ = (x);                                                          \
@@ -389,6 +406,24 @@ int main() {
       printf("phases %s: %.3f ms, %.1f TFLOP/s\n", phase_names[mode], t, fl / (t * 1e-3) / 1e12);
     }
     CHECK(hipFree(src));
+  }
+  {
+    const int T = 1024, iters = 64, wgs = 2048;
+    float* acc;
+    CHECK(hipMalloc(&acc, size_t(T) * 8192 * 4));
+    CHECK(hipMemset(acc, 0, size_t(T) * 8192 * 4));
+    const char* atomic_names[] = {"fp32 atomic add, spread tiles", "fp32 atomic add, one tile at a time",
+                                  "plain stores, spread tiles"};
+    for (int mode = 0; mode < 3; ++mode) {
+      const float t = timeit([&] {
+        if (mode == 0) hipLaunchKernelGGL(k_atomic<0>, dim3(wgs), dim3(256), 0, 0, acc, T, iters);
+        else if (mode == 1) hipLaunchKernelGGL(k_atomic<1>, dim3(wgs), dim3(256), 0, 0, acc, T, iters);
+        else hipLaunchKernelGGL(k_atomic<2>, dim3(wgs), dim3(256), 0, 0, acc, T, iters);
+      });
+      printf("accumulate %s: %.3f ms, %.2f TB/s of float32 added\n", atomic_names[mode], t,
+             double(wgs) * iters * 32768.0 / (t * 1e-3) / 1e12);
+    }
+    CHECK(hipFree(acc));
   }
   CHECK(hipFree(out));
   return 0;
