@@ -425,7 +425,8 @@ template <int D>
 hipError_t fwd_d(const Params& p, hipStream_t st) {
   const int64_t grid = query_tiles(p);
   if (grid == 0) return hipSuccess;
-#define RA_L(C, B, S) hipLaunchKernelGGL((fwd_f32_kernel<D, C, B, S>), dim3(grid), dim3(kThreads), 0, st, p)
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+#define RA_L(C, B, S) hipLaunchKernelGGL((fwd_f32_kernel<D, C, B, S>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
   RA_F32_FLAGS(RA_L);
 #undef RA_L
   return hipGetLastError();
@@ -434,7 +435,8 @@ template <int D>
 hipError_t dkdv_d(const Params& p, hipStream_t st) {
   const int64_t grid = static_cast<int64_t>(p.n_ring) * ((p.Lb + kRows - 1) / kRows) * p.B * p.H;
   if (grid == 0) return hipSuccess;
-#define RA_L(C, B, S) hipLaunchKernelGGL((dkdv_f32_kernel<D, C, B, S>), dim3(grid), dim3(kThreads), 0, st, p)
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+#define RA_L(C, B, S) hipLaunchKernelGGL((dkdv_f32_kernel<D, C, B, S>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
   RA_F32_FLAGS(RA_L);
 #undef RA_L
   return hipGetLastError();
@@ -443,7 +445,8 @@ template <int D>
 hipError_t dq_d(const Params& p, hipStream_t st) {
   const int64_t grid = query_tiles(p);
   if (grid == 0) return hipSuccess;
-#define RA_L(C, B, S) hipLaunchKernelGGL((dq_f32_kernel<D, C, B, S>), dim3(grid), dim3(kThreads), 0, st, p)
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+#define RA_L(C, B, S) hipLaunchKernelGGL((dq_f32_kernel<D, C, B, S>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p)
   RA_F32_FLAGS(RA_L);
 #undef RA_L
   return hipGetLastError();
