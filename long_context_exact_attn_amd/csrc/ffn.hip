@@ -306,9 +306,9 @@ hipError_t ffn_backward(const __bf16* x, const __bf16* w1, const __bf16* w3, con
                         char* ws, hipStream_t st) {
   if (tokens == 0) {
     // no token contributes: the weight gradients are zero
-    RA_HIP(hipMemsetAsync(dw1, 0, sizeof(float) * f * d, st));
-    RA_HIP(hipMemsetAsync(dw3, 0, sizeof(float) * f * d, st));
-    RA_HIP(hipMemsetAsync(dw2, 0, sizeof(float) * d * f, st));
+    RA_HIP(launch_fill_zero(dw1, static_cast<int64_t>(f) * d, st));
+    RA_HIP(launch_fill_zero(dw3, static_cast<int64_t>(f) * d, st));
+    RA_HIP(launch_fill_zero(dw2, static_cast<int64_t>(d) * f, st));
     return hipSuccess;
   }
   const FfnWorkspace w = ffn_workspace(tokens, d, f, chunk, true);

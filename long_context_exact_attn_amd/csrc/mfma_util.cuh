@@ -101,6 +101,9 @@ __device__ __forceinline__ bf16x8 lds_read_a_transposed_swz(const __bf16* tile, 
 // issued through inline assembly so that the compiler does not treat it as an LDS
 // store: it would otherwise wait for every copy in flight before any LDS read and at
 // every barrier.  Callers wait with RA_WAIT_VMCNT and a barrier before the data is read.
+// The copy's LDS address goes through M0, which the statement writes and declares clobbered.  The
+// compiler treats M0 as reserved and would not restore a value of its own there; these kernels rely
+// on it keeping none (tests/test_device_asm.py checks the generated code for any other M0 use).
 __device__ __forceinline__ void dma16(const void* g, __bf16* lds) {
   const unsigned dst = static_cast<unsigned>(
       reinterpret_cast<size_t>((__attribute__((address_space(3))) void*)lds));

@@ -392,8 +392,14 @@ static int bwd_full(const void* q, const void* k, const void* v, const float* bi
     return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes_given,
                 workspace ? "" : " (NULL)");
   if (workspace && !aligned(workspace, 4)) return fail(RA_ERR_WORKSPACE, "workspace is not 4-byte aligned");
-  if (c.kv_elems == 0 && c.q_elems == 0) return ok();
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (c.kv_elems == 0 && c.q_elems == 0) {
+    // no pair at all: the bias gradient is zero
+    if (dbias)
+      RA_TRY(hip_status(ra::launch_fill_zero(dbias, static_cast<int64_t>(shape->heads) * shape->bias_len, st),
+                        "dbias clear"));
+    return ok();
+  }
   c.p.out = const_cast<void*>(out);
   c.p.delta_out = static_cast<float*>(workspace);
   c.p.delta = static_cast<const float*>(workspace);
@@ -407,7 +413,8 @@ static int bwd_full(const void* q, const void* k, const void* v, const float* bi
   if (dbias) {
     if (c.kv_elems == 0 || c.rows == 0) {
       // nothing visible: dbias is zero (the key sums were not written)
-      RA_TRY(hip_status(hipMemsetAsync(dbias, 0, sizeof(float) * shape->heads * shape->bias_len, st), "dbias clear"));
+      RA_TRY(hip_status(ra::launch_fill_zero(dbias, static_cast<int64_t>(shape->heads) * shape->bias_len, st),
+                        "dbias clear"));
     } else {
       RA_TRY(hip_status(ra::launch_bias_grad(c.p.dbias_keys, dbias, shape->batch, shape->heads, shape->kv_len,
                                              shape->bias_len, st),

@@ -208,5 +208,7 @@ hipError_t launch_bias_grad(const float* key_sums, float* dbias, int B, int H, i
                             hipStream_t st);
 hipError_t launch_bias_grad_block(const float* key_sums, float* dbias, int B, int H, int64_t Lb, int64_t kv_pos0,
                                   int64_t bias_len, int accumulate, hipStream_t st);
+// p[0 .. n) = 0 with a kernel (no memset node when the caller captures a graph)
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 }  // namespace ra

@@ -1,6 +1,7 @@
 // One-lane-per-row kernels of libra_attn, for both dtypes: the backward preprocess
 // Delta = rowsum(dO * O), the ring-step finalize and merge, the float32-to-output conversion of
-// gradient sums, and the fixed-order reductions that form the bias gradient from per-key sums.
+// gradient sums, the fixed-order reductions that form the bias gradient from per-key sums, and a
+// zero fill (a kernel, not a memset, so that a caller may capture the call in a HIP graph).
 #include "ra_common.cuh"
 
 namespace ra {
@@ -183,12 +184,26 @@ __global__ __launch_bounds__(256) void bias_grad_block_kernel(const float* __res
   dbias[i] = accumulate ? dbias[i] + acc : acc;
 }
 
+// p[0 .. n) = 0 (grid-stride)
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
+}
+
 hipError_t launch_bias_grad_block(const float* key_sums, float* dbias, int B, int H, int64_t Lb, int64_t kv_pos0,
                                   int64_t bias_len, int accumulate, hipStream_t st) {
   const int64_t n = static_cast<int64_t>(H) * bias_len;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(bias_grad_block_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, key_sums,
                      dbias, B, H, Lb, kv_pos0, bias_len, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)), dim3(256), 0, st,
+                     p, n);
   return hipGetLastError();
 }
 

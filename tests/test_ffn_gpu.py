@@ -69,7 +69,9 @@ def test_ffn_chunking_changes_only_rounding(gpu):
 def test_ffn_empty_and_errors(gpu):
     x, w1, w3, w2, dout = _inputs(0, 64, 96, seed=1, dev=gpu)
     assert ra.blockwise_ffn_fwd(x, w1, w3, w2, chunk=16).shape == (0, 64)
-    dx, dw1, dw3, dw2 = ra.blockwise_ffn_bwd(x, w1, w3, w2, dout, chunk=16)
+    # no token contributes: the weight gradients are cleared, whatever the buffers held
+    dws = [torch.full(w.shape, 7.0, dtype=torch.float32, device=gpu) for w in (w1, w3, w2)]
+    dx, dw1, dw3, dw2 = ra.blockwise_ffn_bwd(x, w1, w3, w2, dout, chunk=16, dw1=dws[0], dw3=dws[1], dw2=dws[2])
     torch.cuda.synchronize()
     assert dx.shape == (0, 64) and not dw1.any() and not dw3.any() and not dw2.any()
     x, w1, w3, w2, dout = _inputs(8, 64, 96, seed=2, dev=gpu)

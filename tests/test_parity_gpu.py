@@ -288,6 +288,12 @@ def test_empty_inputs(gpu):
     q = torch.empty(1, 0, 2, 64, dtype=torch.bfloat16, device=gpu)
     out, lse = ra.blockwise_attn_fwd(q, q, q, n_ring=4, q_chunk=1, k_chunk=1, causal=True)
     assert out.shape == q.shape
+    # no pair is visible: the bias gradient is cleared, whatever its buffer held
+    bias = torch.ones(2, 40, dtype=torch.float32, device=gpu)
+    dbias = torch.full_like(bias, 7.0)
+    ra.blockwise_attn_bwd_dbias(q, q, q, out, lse, q, bias, n_ring=4, q_chunk=1, k_chunk=1, causal=True, dbias=dbias)
+    torch.cuda.synchronize()
+    assert not dbias.any()
 
 
 def test_errors_surface_as_exceptions(gpu):
