@@ -1,7 +1,9 @@
 """The allocation-free backward (ra_blockwise_attn_bwd_noalloc, Delta in the library's static device
 scratch) against the ordinary backward (ra_blockwise_attn_bwd, Delta in a caller workspace) and the
 oracle: two calls in a row on one GPU, the second with a smaller input, so the second reuses what
-the first left in the scratch array."""
+the first left in the scratch array.  The same call captured in a HIP graph (torch.cuda.CUDAGraph) must
+reproduce the eager gradients bit for bit on every replay, with eager work between replays that leaves
+other values in the scratch array and overwrites the outputs."""
 import numpy as np
 import pytest
 import torch
@@ -55,3 +57,41 @@ def test_noalloc_rejects_sizes_over_its_scratch(gpu):
     rc = lib.ra_blockwise_attn_bwd_noalloc(*([None] * 5), 1, 1, 1, 1, *([None] * 6), ctypes.byref(s), None)
     assert rc == -4 and b"4,194,304" in lib.ra_noalloc_last_error()
     del q
+
+
+def test_noalloc_backward_replays_in_a_graph(gpu):
+    w = W.small("noalloc-graph", batch=1, heads=2, kv_len=2048, n_ring=2, bias_len=64, segments="docs",
+                doc_len=(100, 700), backward=True, seed=13)
+    other = W.small("noalloc-graph-other", batch=2, heads=3, kv_len=1536, n_ring=3, backward=True, seed=14)
+    t, u = P.make(w, gpu), P.make(other, gpu)
+    out, lse = P.gpu_forward(w, t)
+    out_u, lse_u = P.gpu_forward(other, u)
+    kw = dict(n_ring=w.n_ring, q_chunk=w.q_chunk, k_chunk=w.k_chunk, causal=w.causal, ring_rank=w.ring_rank)
+    kw_u = dict(n_ring=other.n_ring, q_chunk=other.q_chunk, k_chunk=other.k_chunk, causal=other.causal,
+                ring_rank=other.ring_rank)
+    args = (t["q"], t["k"], t["v"], out, lse, t["dout"], t["bias"], t["segment_ids"])
+    args_u = (u["q"], u["k"], u["v"], out_u, lse_u, u["dout"], u["bias"], u["segment_ids"])
+    grads = [torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])]
+    grads_u = [torch.empty_like(u["q"]), torch.empty_like(u["k"]), torch.empty_like(u["v"])]
+
+    # eager call first (it also looks up the scratch array's device address, outside any capture)
+    ra.blockwise_attn_bwd_noalloc(*args, **kw, dq=grads[0], dk=grads[1], dv=grads[2])
+    torch.cuda.synchronize()
+    ref = [g.clone() for g in grads]
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ra.blockwise_attn_bwd_noalloc(*args, **kw, dq=grads[0], dk=grads[1], dv=grads[2])
+    torch.cuda.synchronize()
+
+    for i in range(4):
+        print("replay", i, flush=True)
+        for g in grads:
+            g.fill_(float("nan"))
+        # another shape through the same scratch array, eagerly
+        ra.blockwise_attn_bwd_noalloc(*args_u, **kw_u, dq=grads_u[0], dk=grads_u[1], dv=grads_u[2])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, g, r in zip(("dq", "dk", "dv"), grads, ref):
+            assert torch.equal(g, r), f"replay {i}: {name} differs from the eager call"
