@@ -1,5 +1,5 @@
 // Issue-rate microbenchmarks for gfx950, used to set the ceilings the attention kernels are
-// judged against: sustained v_mfma_f32_32x32x16_bf16 throughput, cycles per wave64
+// measured against: sustained v_mfma_f32_32x32x16_bf16 throughput, cycles per wave64
 // instruction of v_exp_f32, v_fma_f32, v_dot2_f32_bf16 and v_max, and whether exponentials
 // issued between matrix products of one wave overlap them, and LDS read bandwidth.  Every thread writes one float
 // of `out` (sized for the largest grid); nothing else is read or written.
