@@ -272,3 +272,79 @@ def test_bwd_step_errors(gpu):
     qf = t["q"].float()
     with pytest.raises(ra.RAError, match="RA_BF16"):
         ra.blockwise_attn_bwd_step(qf, qf, qf, lse, lse, qf, q_pos0=0, kv_pos0=0, causal=True)
+
+
+# ------------------------------------------------------------------ seeded random sweep of the ring steps
+STEP_SEED = 20261204
+N_STEP_CASES = 16
+STEP_MAX_PAIRS = 1 << 23   # batch * heads * kv_len^2 per case (all ranks of the ring), so the oracle stays in seconds
+
+
+def step_sweep_cases(seed=STEP_SEED, n=N_STEP_CASES):
+    """Seeded random shapes for the ring-step entry points (bfloat16, as the steps are): every rank
+    of a ring on one GPU, blocks of any length (ragged included), head_dim 64 or 128, no causal mask,
+    token-level or block-level causality, a bias of any length, segment ids sorted or scattered; plus
+    the rank whose forward step chain is checked.  Pure host logic."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        i = len(cases)
+        head_dim = int(rng.choice([64, 128]))
+        batch = int(rng.integers(1, 3))
+        heads = int(rng.integers(1, 4))
+        n_ring = int(rng.choice([2, 3, 4, 8]))
+        if rng.random() < 0.4:
+            lb = int(rng.integers(1, 1024 // n_ring + 1))
+        else:
+            lb = int(rng.choice([64, 128, 200, 256]))
+        lb = max(1, min(lb, 2048 // n_ring))
+        kv_len = n_ring * lb
+        if batch * heads * kv_len * kv_len > STEP_MAX_PAIRS:
+            continue
+        divs = [d for d in range(2, lb + 1) if lb % d == 0]
+        u = rng.random()
+        causal = False if u < 0.25 else (True if (u < 0.7 or not divs) else int(rng.choice(divs)))
+        bias_len = 0 if rng.random() < 0.4 else int(rng.integers(1, 2 * kv_len + 2))
+        segments = str(rng.choice(["none", "docs", "scattered"]))
+        lo = int(rng.integers(1, max(2, kv_len // 4) + 1))
+        doc_len = (lo, int(rng.integers(lo, max(lo, kv_len // 2) + 1)))
+        rank = int(rng.integers(0, n_ring))
+        w = W.small(f"steps{i:02d}", batch=batch, heads=heads, head_dim=head_dim, kv_len=kv_len, n_ring=n_ring,
+                    causal=causal, bias_len=bias_len, segments=segments, doc_len=doc_len, backward=True,
+                    seed=int(rng.integers(0, 2**31)))
+        cases.append((w, rank))
+    return cases
+
+
+STEP_CASES = step_sweep_cases()
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=[c[0].name for c in STEP_CASES])
+def test_step_sweep(gpu, case):
+    w, r = case
+    print("case", w, "rank", r, flush=True)
+    t = P.make(w, gpu)
+    lb = w.block_len
+    rows = slice(r * lb, (r + 1) * lb)
+    # forward: rank r's query block folds in every K/V block in ring order, then finalizes
+    wr = W.replace(w, ring_rank=r)
+    tr = dict(t, q=t["q"][:, rows].contiguous())
+    out_r, lse_r = ra.blockwise_attn_fwd_finalize(_chain(wr, tr, _ring_order(wr)))
+    # backward: every rank, dQ sums staying with the queries, dK / dV (and with a bias the per-key sums
+    # of dS) travelling with their block
+    out, lse = P.gpu_forward(w, t)
+    res = _ring_backward(w, t, out, lse, with_dbias=t["bias"] is not None)
+    torch.cuda.synchronize()
+    d = P.oracle_inputs(t)
+    import oracle
+    ref_o, ref_l = P.oracle_forward(w, d, w.q_positions())
+    P.assert_close(f"{w.name} rank {r} steps", P.np64(out_r), ref_o[:, rows], "bf16", strict=False)
+    P.assert_lse(lse_r.cpu().numpy().astype(np.float64), ref_l[:, :, rows], "bf16")
+    rdq, rdk, rdv, _ = oracle.backward(d["q"], d["k"], d["v"], d["dout"], q_pos=w.q_positions(), causal=w.causal,
+                                       bias=d["bias"], segment_ids=d["segment_ids"])
+    for gname, g, ref in zip(("dq", "dk", "dv"), res[:3], (rdq, rdk, rdv)):
+        P.assert_close(f"{w.name} {gname} steps", P.np64(g), ref, "bf16", strict=False)
+    if t["bias"] is not None:
+        ref_db = oracle.bias_grad(d["q"], d["k"], d["v"], d["dout"], q_pos=w.q_positions(), causal=w.causal,
+                                  bias=d["bias"], segment_ids=d["segment_ids"])
+        P.assert_close_sums(f"{w.name} dbias steps", res[3].double().cpu().numpy(), ref_db)
