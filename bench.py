@@ -208,6 +208,18 @@ class ClockSampler:
                                      "max": during[-1]} if during else None)}
 
 
+def copy_probe(mib, dev):
+    """One device copy of mib MiB (mib MiB read, mib MiB written): the reference dispatch against which
+    a profiler's HBM byte counters are calibrated in the same run."""
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy probe: {mib} MiB read + {mib} MiB written", file=sys.stderr)
+    del src, dst
+
+
 def bench_ffn(args):
     """The blockwise feed-forward on one device's share of the 1M-token context (131072 tokens of the
     1024-wide model, LLaMA's d_ff rule: 8/3 * 1024 rounded up to a multiple of 256 = 2816)."""
@@ -238,6 +250,8 @@ def bench_ffn(args):
         if ev is not None:
             ev[2].record()
 
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -364,12 +378,7 @@ def main():
         mark(4)
 
     if args.copy_probe_mib:
-        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written", file=sys.stderr)
-        del src, dst
+        copy_probe(args.copy_probe_mib, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
