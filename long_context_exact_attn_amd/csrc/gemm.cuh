@@ -227,11 +227,17 @@ __global__ __launch_bounds__(kThreadsG) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
+  // one wave-uniform branch per tile between the all-fast and the checked copies: with the choice made
+  // inside the unrolled per-copy loop the compiler kept a pair of branches around every copy
   auto issue = [&](int kt, int slot) {
     const int64_t k0 = kbeg + static_cast<int64_t>(kt) * BK;
-    const bool fast = rows_in && k0 + BK <= kend;
-    copy_tile<A_KMAJ, BM>(A, k0, kend, sA[slot], wave, lane, offA, fast, arow);
-    copy_tile<B_KMAJ, BN>(B, k0, kend, sB[slot], wave, lane, offB, fast, brow);
+    if (rows_in && k0 + BK <= kend) {
+      copy_tile<A_KMAJ, BM>(A, k0, kend, sA[slot], wave, lane, offA, true, arow);
+      copy_tile<B_KMAJ, BN>(B, k0, kend, sB[slot], wave, lane, offB, true, brow);
+    } else {
+      copy_tile<A_KMAJ, BM>(A, k0, kend, sA[slot], wave, lane, offA, false, arow);
+      copy_tile<B_KMAJ, BN>(B, k0, kend, sB[slot], wave, lane, offB, false, brow);
+    }
   };
 
   constexpr int PER_TILE = TA::PER + TB::PER;   // copies per lane and tile
