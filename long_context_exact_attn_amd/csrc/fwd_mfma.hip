@@ -237,13 +237,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     const __bf16* kb = kp + kv_bh + static_cast<int64_t>(key0) * kstride;
     const __bf16* vb = vp + kv_bh + static_cast<int64_t>(key0) * kstride;
     if constexpr (kUniformCopies) {
-      const bool full = key0 + BK <= kend;
-      const int nvalid = kend - key0;
+      // full tiles (all but a block's ragged last one) take a branch of their own, so their copies
+      // need no per-chunk selects (forward -1.6% on the 1M-token share; the same in dK/dV and dQ
+      // measured slower)
+      if (key0 + BK <= kend) {
 #pragma unroll
-      for (int j = 0; j < NSEG; ++j) {
-        const unsigned off = 2u * static_cast<unsigned>(full ? goff[j] : (grow_[j] < nvalid ? goff[j] : goff0[j]));
-        dma16_sb(kb, off, &sK[slot][(wave * NSEG + j) * 512]);
-        dma16_sb(vb, off, &sV[slot][(wave * NSEG + j) * 512]);
+        for (int j = 0; j < NSEG; ++j) {
+          const unsigned off = 2u * static_cast<unsigned>(goff[j]);
+          dma16_sb(kb, off, &sK[slot][(wave * NSEG + j) * 512]);
+          dma16_sb(vb, off, &sV[slot][(wave * NSEG + j) * 512]);
+        }
+      } else {
+        const int nvalid = kend - key0;
+#pragma unroll
+        for (int j = 0; j < NSEG; ++j) {
+          const unsigned off = 2u * static_cast<unsigned>(grow_[j] < nvalid ? goff[j] : goff0[j]);
+          dma16_sb(kb, off, &sK[slot][(wave * NSEG + j) * 512]);
+          dma16_sb(vb, off, &sV[slot][(wave * NSEG + j) * 512]);
+        }
       }
     } else {
       const bool full = key0 + BK <= kend;
