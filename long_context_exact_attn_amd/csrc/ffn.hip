@@ -96,34 +96,22 @@ struct GateFwd {
 // with dh = dout W2 already in DH [M, f] and s = sigmoid(g),
 //   dg = dh u s (1 + g (1 - s)),  du = dh g s   into DGDU [M, 2 f] (g's columns, then u's)
 //   h = g s u                                   into H [M, f]
-// so g and u never leave the registers.  One row at a time, four hidden units per access; the row's
-// dh values are all loaded before any result is stored (the pointers are declared not to alias, so
-// the loads overlap).
-__device__ __forceinline__ void gate_bwd_row(const __bf16* __restrict__ DH, __bf16* __restrict__ DGDU,
-                                             __bf16* __restrict__ H, const f32x16 (&acc)[2], int64_t m, int64_t j0,
-                                             int64_t f) {
-  bf16x4 dh[4];
+// so g and u never leave the registers.  Four hidden units per access.
+//
+// The wave's results for one row m and four hidden units j .. j + 3 from its g and u accumulators
+__device__ __forceinline__ void gate_bwd_units(__bf16* __restrict__ DGDU, __bf16* __restrict__ H, const f32x16 (&acc)[2],
+                                               int g, bf16x4 dh, int64_t m, int64_t j, int64_t f) {
+  bf16x4 dg, du, h;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int64_t j = j0 + 8 * g;
-    dh[g] = j < f ? *reinterpret_cast<const bf16x4*>(DH + m * f + j) : bf16x4{};
+  for (int e = 0; e < 4; ++e) {
+    const float gv = acc[0][4 * g + e], uv = acc[1][4 * g + e], sv = sigmoidf_(gv), d = (float)dh[e];
+    dg[e] = (__bf16)(d * uv * sv * (1.f + gv * (1.f - sv)));
+    du[e] = (__bf16)(d * gv * sv);
+    h[e] = (__bf16)(gv * sv * uv);
   }
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int64_t j = j0 + 8 * g;
-    if (j >= f) continue;
-    bf16x4 dg, du, h;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float gv = acc[0][4 * g + e], uv = acc[1][4 * g + e], sv = sigmoidf_(gv), d = (float)dh[g][e];
-      dg[e] = (__bf16)(d * uv * sv * (1.f + gv * (1.f - sv)));
-      du[e] = (__bf16)(d * gv * sv);
-      h[e] = (__bf16)(gv * sv * uv);
-    }
-    *reinterpret_cast<bf16x4*>(DGDU + m * 2 * f + j) = dg;
-    *reinterpret_cast<bf16x4*>(DGDU + m * 2 * f + f + j) = du;
-    *reinterpret_cast<bf16x4*>(H + m * f + j) = h;
-  }
+  *reinterpret_cast<bf16x4*>(DGDU + m * 2 * f + j) = dg;
+  *reinterpret_cast<bf16x4*>(DGDU + m * 2 * f + f + j) = du;
+  *reinterpret_cast<bf16x4*>(H + m * f + j) = h;
 }
 
 struct GateBwd {
@@ -133,10 +121,37 @@ struct GateBwd {
   int64_t f;
   __device__ void operator()(const f32x16 (&acc)[4][2], int64_t mb0, int64_t nb0, int, int l32, int hh, int64_t M,
                              int64_t) const {
+    const int64_t j0 = nb0 / 2 + 4 * hh;   // the lane's first hidden unit; it owns j0 + 8 g + 0..3
+    if (mb0 + 128 <= M && nb0 / 2 + 32 <= f) {
+      // the wave's 128 rows and 32 hidden units are all inside: every dh load is issued before the first
+      // store, with no branch in between.  (Stores count in the same counter as loads; with a branch
+      // around each load, the wait for a row's dh also waited for every store issued before it.)
+      bf16x4 dh[4][4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          dh[a][g] = *reinterpret_cast<const bf16x4*>(DH + (mb0 + 32 * a + l32) * f + j0 + 8 * g);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) gate_bwd_units(DGDU, H, acc[a], g, dh[a][g], mb0 + 32 * a + l32, j0 + 8 * g, f);
+      return;
+    }
+    // a ragged tile: rows past M and hidden units past f are left out, one row at a time
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int64_t m = mb0 + 32 * a + l32;
-      if (m < M) gate_bwd_row(DH, DGDU, H, acc[a], m, nb0 / 2 + 4 * hh, f);
+      if (m >= M) continue;
+      bf16x4 dh[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t j = j0 + 8 * g;
+        dh[g] = j < f ? *reinterpret_cast<const bf16x4*>(DH + m * f + j) : bf16x4{};
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (j0 + 8 * g < f) gate_bwd_units(DGDU, H, acc[a], g, dh[g], m, j0 + 8 * g, f);
     }
   }
 };
