@@ -38,6 +38,8 @@ CASES = [
     ("one-chunk", 512, 128, 352, 4096),
     ("chunk-1-token", 5, 64, 96, 1),
     ("wide", 1536, 512, 1408, 512),
+    # d_ff 200: one wave's 32 hidden units straddle the end; d_model 136: a ragged K step; 777 = 2 x 300 + 177
+    ("ragged-hidden", 777, 136, 200, 300),
 ]
 
 
