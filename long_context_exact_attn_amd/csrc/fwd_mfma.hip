@@ -72,15 +72,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- which query tile: heads/batches vary fastest so that consecutive workgroups,
-  // which the dispatcher spreads round-robin over the XCDs, keep one head per XCD
-  // when B*H is a multiple of 8; the heaviest (latest) query tiles go first.
-  const int HB = p.B * p.H;
+  // ---- which query tile: tasks are numbered head-major, each head's heaviest (latest) query
+  // tiles first, and every XCD takes a contiguous range of them, so the workgroups resident on
+  // one XCD stream the same head's K/V through its L2 (grid = B * H * n_qt)
   const int64_t n_qt_blk = (p.Lb + BQ - 1) / BQ;
   const int64_t n_qt = (p.ring_rank < 0 ? p.n_ring : 1) * n_qt_blk;
-  const int64_t wg = blockIdx.x;
-  const int hb = static_cast<int>(wg % HB);
-  const int64_t t = n_qt - 1 - wg / HB;
+  const int64_t task = xcd_task(blockIdx.x, gridDim.x);
+  const int hb = static_cast<int>(task / n_qt);
+  const int64_t t = n_qt - 1 - task % n_qt;
   const int b = hb / p.H, h = hb % p.H;
   const int r_local = static_cast<int>(t / n_qt_blk);
   const int64_t qa = (t % n_qt_blk) * BQ;                  // first row of the tile inside its block

@@ -93,6 +93,19 @@ __device__ __forceinline__ int causal_first_query(int rel, int off, int c) {
   return (g / c) * c - off;
 }
 
+// ---------------------------------------------------------------- workgroup order
+// The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn (XCD id % 8), and each XCD has
+// an L2 of its own.  The task of workgroup `id` in a grid of `grid`: XCD x takes the contiguous range of
+// tasks that starts at x * (grid / 8) + min(x, grid % 8), in order.  With tasks numbered head-major, the
+// workgroups an XCD holds at once then belong to one head and stream the same K/V (or Q and dO) through
+// its L2.  A bijection of [0, grid) for any grid size.
+__device__ __forceinline__ int64_t xcd_task(int64_t id, int64_t grid) {
+  const int x = static_cast<int>(id & 7);
+  const int64_t per = grid >> 3;
+  const int rem = static_cast<int>(grid & 7);
+  return x * per + (x < rem ? x : rem) + (id >> 3);
+}
+
 // ---------------------------------------------------------------- forward-direction ring walk
 // Walks the K/V tiles one query tile must visit, in ring order, tile size BK.
 // Start with begin(); each next() moves to the following tile and returns
