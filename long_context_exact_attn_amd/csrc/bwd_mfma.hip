@@ -66,13 +66,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // tile order as in the forward: head-major tasks, each head's heaviest query tiles first, a
-  // contiguous range of them per XCD (grid = B * H * n_qt)
+  // tile order (grid = B * H * n_qt): the heaviest query tiles of a head first; one (batch, head) per
+  // XCD at a time for one rank's queries (or one ring step), whose tiles carry similar work, pairs
+  // fastest for the whole ring, where a causal mask makes the work fall from tile to tile (measured
+  // both ways on each kind of launch)
   const int64_t n_qt_blk = (p.Lb + BQ - 1) / BQ;
   const int64_t n_qt = (p.ring_rank < 0 ? p.n_ring : 1) * n_qt_blk;
-  const int64_t task = xcd_task(blockIdx.x, gridDim.x);
-  const int hb = static_cast<int>(task / n_qt);
-  const int64_t t = n_qt - 1 - task % n_qt;
+  const HeadTile ht = head_tile(blockIdx.x, p.B * p.H, n_qt, p.ring_rank >= 0);
+  const int hb = ht.hb;
+  const int64_t t = n_qt - 1 - ht.t;
   const int b = hb / p.H, h = hb % p.H;
   const int r_local = static_cast<int>(t / n_qt_blk);
   const int64_t qa = (t % n_qt_blk) * BQ;
@@ -493,14 +495,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // head-major tasks, each head's key tiles of block 0 first (under a causal mask they meet the
-  // most query blocks), a contiguous range of them per XCD, so the workgroups resident on one XCD
-  // stream the same head's Q and dO through its L2 (grid = B * H * n_ring * n_kt_blk)
+  // grid = B * H * n_ring * n_kt_blk: a head's key tiles of block 0 first (under a causal mask they
+  // meet the most query blocks); one (batch, head) per XCD at a time for one rank's queries (or one
+  // ring step), pairs fastest for the whole ring, as in the dQ kernel
   const int64_t n_kt_blk = (p.Lb + BKW - 1) / BKW;
-  const int64_t n_kt = static_cast<int64_t>(p.n_ring) * n_kt_blk;
-  const int64_t task = xcd_task(blockIdx.x, gridDim.x);
-  const int hb = static_cast<int>(task / n_kt);
-  const int64_t kt = task % n_kt;
+  const HeadTile ht = head_tile(blockIdx.x, p.B * p.H, static_cast<int64_t>(p.n_ring) * n_kt_blk,
+                                p.ring_rank >= 0);
+  const int hb = ht.hb;
+  const int64_t kt = ht.t;
   const int b = hb / p.H, h = hb % p.H;
   const int j = static_cast<int>(kt / n_kt_blk);
   const int64_t ka = (kt % n_kt_blk) * BKW;                     // first key of the tile inside block j

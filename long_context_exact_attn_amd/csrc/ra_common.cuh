@@ -94,16 +94,26 @@ __device__ __forceinline__ int causal_first_query(int rel, int off, int c) {
 }
 
 // ---------------------------------------------------------------- workgroup order
-// The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn (XCD id % 8), and each XCD has
-// an L2 of its own.  The task of workgroup `id` in a grid of `grid`: XCD x takes the contiguous range of
-// tasks that starts at x * (grid / 8) + min(x, grid % 8), in order.  With tasks numbered head-major, the
-// workgroups an XCD holds at once then belong to one head and stream the same K/V (or Q and dO) through
-// its L2.  A bijection of [0, grid) for any grid size.
-__device__ __forceinline__ int64_t xcd_task(int64_t id, int64_t grid) {
-  const int x = static_cast<int>(id & 7);
-  const int64_t per = grid >> 3;
-  const int rem = static_cast<int>(grid & 7);
-  return x * per + (x < rem ? x : rem) + (id >> 3);
+// The (batch, head) pair hb and the tile t of workgroup `id`, for HB pairs of n_t tiles each (the grid
+// is HB * n_t; tile 0 of a pair is its first to run).  The dispatcher hands consecutive workgroup ids to
+// the 8 XCDs in turn (XCD id % 8), and each XCD has an L2 of its own.
+// - by_pair (only when HB is a multiple of 8): XCD x takes the pairs x, x + 8, x + 16, ... one after
+//   the other, all tiles of a pair before the next.  The workgroups an XCD holds at once then belong to
+//   one pair and stream the same K/V (or Q and dO) through its L2, and every XCD still gets pairs of
+//   every batch row.
+// - otherwise pairs vary fastest, so an XCD holds tiles of HB / 8 pairs at once.
+// (32-bit arithmetic: the host keeps every grid below 2^31 workgroups.)
+struct HeadTile {
+  int hb;
+  int64_t t;
+};
+__device__ __forceinline__ HeadTile head_tile(unsigned id, int HB, int64_t n_t, bool by_pair) {
+  const unsigned nt = static_cast<unsigned>(n_t), hbs = static_cast<unsigned>(HB);
+  if (by_pair && (hbs & 7u) == 0) {
+    const unsigned i = id >> 3;
+    return {static_cast<int>((id & 7u) + 8u * (i / nt)), static_cast<int64_t>(i % nt)};
+  }
+  return {static_cast<int>(id % hbs), static_cast<int64_t>(id / hbs)};
 }
 
 // ---------------------------------------------------------------- forward-direction ring walk
