@@ -247,4 +247,21 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Host side of the backward launchers: calls CALL(causal mode, has bias, has segment ids) with the
+// template flags that match the parameters.
+#define RA_SELECT_FLAGS(CALL)                                                      \
+  do {                                                                             \
+    const bool b_ = p.bias != nullptr, s_ = p.seg != nullptr;                     \
+    if (p.causal == 1) {                                                           \
+      if (b_) { if (s_) CALL(1, true, true); else CALL(1, true, false); }          \
+      else { if (s_) CALL(1, false, true); else CALL(1, false, false); }           \
+    } else if (p.causal > 1) {                                                     \
+      if (b_) { if (s_) CALL(2, true, true); else CALL(2, true, false); }          \
+      else { if (s_) CALL(2, false, true); else CALL(2, false, false); }           \
+    } else {                                                                       \
+      if (b_) { if (s_) CALL(0, true, true); else CALL(0, true, false); }          \
+      else { if (s_) CALL(0, false, true); else CALL(0, false, false); }           \
+    }                                                                              \
+  } while (0)
+
 }  // namespace ra
