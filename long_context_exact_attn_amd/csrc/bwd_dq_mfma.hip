@@ -201,16 +201,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
       }
     }
   };
+  // head_dim 64 without bias or segment ids: copies from the tile's wave-uniform base plus each lane's fixed
+  // offset, full tiles in a branch of their own (no per-chunk selects); measured, as for the forward
+  constexpr bool kUniformCopies = D == 64 && !HAS_BIAS && !HAS_SEG;
   auto issue_kv = [&](int key0, int kend, int slot) {
     const __bf16* kb = kp + kv_bh + static_cast<int64_t>(key0) * kstride;
     const __bf16* vb = vp + kv_bh + static_cast<int64_t>(key0) * kstride;
-    const bool full = key0 + BK <= kend;
-    const int nvalid = kend - key0;
+    if constexpr (kUniformCopies) {
+      if (key0 + BK <= kend) {
 #pragma unroll
-    for (int jj = 0; jj < NSEG; ++jj) {
-      const int off = (full || grow_[jj] < nvalid) ? goff[jj] : goff0[jj];
-      dma16(kb + off, &sK[slot][(wave * NSEG + jj) * 512]);
-      dma16(vb + off, &sV[slot][(wave * NSEG + jj) * 512]);
+        for (int jj = 0; jj < NSEG; ++jj) {
+          const unsigned off = 2u * static_cast<unsigned>(goff[jj]);
+          dma16_sb(kb, off, &sK[slot][(wave * NSEG + jj) * 512]);
+          dma16_sb(vb, off, &sV[slot][(wave * NSEG + jj) * 512]);
+        }
+      } else {
+        const int nvalid = kend - key0;
+#pragma unroll
+        for (int jj = 0; jj < NSEG; ++jj) {
+          const unsigned off = 2u * static_cast<unsigned>(grow_[jj] < nvalid ? goff[jj] : goff0[jj]);
+          dma16_sb(kb, off, &sK[slot][(wave * NSEG + jj) * 512]);
+          dma16_sb(vb, off, &sV[slot][(wave * NSEG + jj) * 512]);
+        }
+      }
+    } else {
+      const bool full = key0 + BK <= kend;
+      const int nvalid = kend - key0;
+#pragma unroll
+      for (int jj = 0; jj < NSEG; ++jj) {
+        const int off = (full || grow_[jj] < nvalid) ? goff[jj] : goff0[jj];
+        dma16(kb + off, &sK[slot][(wave * NSEG + jj) * 512]);
+        dma16(vb + off, &sV[slot][(wave * NSEG + jj) * 512]);
+      }
     }
   };
 

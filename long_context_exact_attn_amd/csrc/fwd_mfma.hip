@@ -236,8 +236,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     const __bf16* vb = vp + kv_bh + static_cast<int64_t>(key0) * kstride;
     if constexpr (kUniformCopies) {
       // full tiles (all but a block's ragged last one) take a branch of their own, so their copies
-      // need no per-chunk selects (forward -1.6% on the 1M-token share; the same in dK/dV and dQ
-      // measured slower)
+      // need no per-chunk selects (-1.6% on the 1M-token share; the dQ kernel does the same)
       if (key0 + BK <= kend) {
 #pragma unroll
         for (int j = 0; j < NSEG; ++j) {
