@@ -223,11 +223,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, O
     if constexpr (kUniformCopies) {
       const bool full = row0 + BQ <= rend;
       const int nvalid = rend - row0;
+      if (!STEP && full) {
+        // full tiles in a branch of their own, with no per-chunk selects (-0.5% on the 1M-token share);
+        // the ring-step variant keeps the selects, without which it no longer fits 256 registers
 #pragma unroll
-      for (int jj = 0; jj < NSEG; ++jj) {
-        const unsigned off = 2u * static_cast<unsigned>(full ? goff[jj] : (grow_[jj] < nvalid ? goff[jj] : goff0[jj]));
-        dma16_sb(qb_, off, &sQ[slot][(wave * NSEG + jj) * 512]);
-        dma16_sb(gb_, off, &sG[slot][(wave * NSEG + jj) * 512]);
+        for (int jj = 0; jj < NSEG; ++jj) {
+          const unsigned off = 2u * static_cast<unsigned>(goff[jj]);
+          dma16_sb(qb_, off, &sQ[slot][(wave * NSEG + jj) * 512]);
+          dma16_sb(gb_, off, &sG[slot][(wave * NSEG + jj) * 512]);
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < NSEG; ++jj) {
+          const unsigned off = 2u * static_cast<unsigned>(full ? goff[jj] : (grow_[jj] < nvalid ? goff[jj] : goff0[jj]));
+          dma16_sb(qb_, off, &sQ[slot][(wave * NSEG + jj) * 512]);
+          dma16_sb(gb_, off, &sG[slot][(wave * NSEG + jj) * 512]);
+        }
       }
     } else {
       const bool full = row0 + BQ <= rend;
