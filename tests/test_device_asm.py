@@ -64,7 +64,8 @@ def test_m0_written_only_by_the_copies(device_asm):
             if ln.strip().startswith(";;#ASMEND"):
                 writes = [i for i, x in enumerate(block) if M0.search(x)]
                 for i in writes:
-                    assert re.fullmatch(r"s_mov_b32 m0, s\d+", block[i]), (name, block)
+                    # the "s" operand may be any scalar register, vcc_lo / vcc_hi included
+                    assert re.fullmatch(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)", block[i]), (name, block)
                     assert any(x.startswith("global_load_lds_dwordx4") for x in block[i + 1:]), (name, block)
                     copies += 1
                 in_asm = False
