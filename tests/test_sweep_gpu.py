@@ -75,9 +75,38 @@ def test_sweep_cases_are_valid():
     assert sweep_cases()[7] == CASES[7]
 
 
+# Workgroup order: with batch * heads a multiple of 8, every kernel of a single rank's share (and the forward
+# of the whole ring) runs the (batch, head) pairs one after the other on each XCD; otherwise pairs vary
+# fastest.  Full tensors of both orders, over several tiles per pair.
+ORDER_CASES = [
+    W.small("order-b2h4-rank1", batch=2, heads=4, kv_len=1024, n_ring=4, ring_rank=1, backward=True, seed=11),
+    W.small("order-b1h16-rank3", batch=1, heads=16, kv_len=1024, n_ring=4, ring_rank=3, backward=True, seed=12),
+    W.small("order-b1h24-ring", batch=1, heads=24, kv_len=512, n_ring=2, ring_rank=-1, backward=True, seed=13),
+    W.small("order-b2h8-d128-rank0-bias", batch=2, heads=8, head_dim=128, kv_len=512, n_ring=2, ring_rank=0,
+            bias_len=96, backward=True, seed=14),
+    W.small("order-b1h12-rank2", batch=1, heads=12, kv_len=1024, n_ring=4, ring_rank=2, backward=True, seed=15),
+]
+
+
+def test_order_cases_are_valid():
+    for w in ORDER_CASES:
+        assert w.batch * w.heads * w.q_len * w.kv_len <= MAX_PAIRS
+    assert {w.batch * w.heads % 8 == 0 for w in ORDER_CASES} == {True, False}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("w", ORDER_CASES, ids=[c.name for c in ORDER_CASES])
+def test_workgroup_order(gpu, w):
+    _check(gpu, w)
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
 def test_sweep(gpu, w):
+    _check(gpu, w)
+
+
+def _check(gpu, w):
     print(w, flush=True)
     t = P.make(w, gpu)
     out, lse = P.gpu_forward(w, t)
