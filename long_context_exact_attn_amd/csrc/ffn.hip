@@ -192,17 +192,18 @@ struct F32Out {
   }
 };
 
-// out (+)= sum over s = 0 .. splits - 1 of part[s] (in that order), rows split over out1 / out2
+// out (+)= sum over s = 0 .. splits - 1 of part[s] (in that order), rows split over out1 / out2; four
+// consecutive columns per thread (N is a multiple of 8 and every pointer 16-byte aligned)
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, float* out1, float* out2,
                                                             int64_t rsplit, int64_t ldo, int64_t M, int64_t N,
                                                             int splits, int accumulate) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
   if (i >= M * N) return;
   const int64_t m = i / N, n = i % N;
   float* o = m < rsplit ? out1 + m * ldo + n : out2 + (m - rsplit) * ldo + n;
-  float s = accumulate ? *o : 0.f;
-  for (int k = 0; k < splits; ++k) s += part[static_cast<int64_t>(k) * M * N + i];
-  *o = s;
+  f32x4 s = accumulate ? *reinterpret_cast<const f32x4*>(o) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < splits; ++k) s += *reinterpret_cast<const f32x4*>(part + static_cast<int64_t>(k) * M * N + i);
+  *reinterpret_cast<f32x4*>(o) = s;
 }
 
 #define RA_HIP(x)                         \
@@ -269,8 +270,8 @@ hipError_t weight_grad(const Operand& A, const Operand& B, int64_t M, int64_t N,
   F32Out epi{out1, out2, rsplit, N, part, splits, accumulate};
   RA_HIP((run<false, false>(A, B, M, N, K, tiles_n, splits, map, epi, st)));
   if (splits > 1) {
-    const int64_t n = M * N;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, part,
+    const int64_t n4 = M * N / 4;   // N is a multiple of 8
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st, part,
                        out1, out2, rsplit, N, M, N, splits, accumulate);
     RA_HIP(hipGetLastError());
   }
