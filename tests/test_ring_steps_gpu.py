@@ -318,8 +318,24 @@ def step_sweep_cases(seed=STEP_SEED, n=N_STEP_CASES):
 
 STEP_CASES = step_sweep_cases()
 
+# batch * heads a multiple of 8: the step kernels then run one (batch, head) per XCD at a time (the
+# random shapes above have at most 6 pairs)
+STEP_ORDER_CASES = [
+    (W.small("steps-order-b2h4", batch=2, heads=4, kv_len=1024, n_ring=4, backward=True, seed=21), 2),
+    (W.small("steps-order-b1h8-d128-bias", batch=1, heads=8, head_dim=128, kv_len=768, n_ring=3, bias_len=200,
+             backward=True, seed=22), 1),
+    (W.small("steps-order-b1h16-blocks", batch=1, heads=16, kv_len=512, n_ring=4, causal=32, backward=True,
+             seed=23), 3),
+]
 
-@pytest.mark.parametrize("case", STEP_CASES, ids=[c[0].name for c in STEP_CASES])
+
+def test_step_order_cases_are_valid():
+    for w, r in STEP_ORDER_CASES:
+        assert w.batch * w.heads % 8 == 0 and 0 <= r < w.n_ring
+        assert w.batch * w.heads * w.kv_len * w.kv_len <= STEP_MAX_PAIRS
+
+
+@pytest.mark.parametrize("case", STEP_CASES + STEP_ORDER_CASES, ids=[c[0].name for c in STEP_CASES + STEP_ORDER_CASES])
 def test_step_sweep(gpu, case):
     w, r = case
     print("case", w, "rank", r, flush=True)
